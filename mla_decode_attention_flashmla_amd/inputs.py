@@ -1,0 +1,214 @@
+"""Seeded synthetic workloads for MLA decode.
+
+This module only draws numbers and lays them out (paged pool, block table,
+sequence lengths).  It holds none of the attention arithmetic, so both the
+HIP path and the CPU oracle can take their inputs from it.
+
+Layout of one workload (all NumPy, host memory):
+
+* ``q``            [B, s_q, H, 576]  bf16 bits as uint16, or float32
+* ``kv_cache``     [num_blocks, 64, 576] same dtype as q (the paged latent pool;
+                   columns 0..511 are the latent part that is also V, 512..575 rope)
+* ``block_table``  [B, max_blocks] int32, -1 where unused
+* ``seqlens``      [B] int32
+* ``scale``        float32 softmax scale
+
+Random streams come from ``numpy.random.SeedSequence(seed).spawn(5)`` in a fixed
+order: sequence lengths, block permutation, Q, KV pool, sharp-peak rows.  Large
+arrays are drawn in fixed 1 Mi-element chunks, each with its own child seed,
+so the bytes do not depend on the number of worker threads.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+PAGE = 64          # tokens per KV block
+D_QK = 576         # latent (512) + rope (64)
+D_V = 512          # V is the first 512 columns of a cache row
+
+_CHUNK = 1 << 20
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and distribution of one synthetic MLA decode workload."""
+
+    name: str
+    batch: int
+    s_q: int
+    heads: int
+    context: int                  # every sequence length, or the upper bound when ragged
+    dtype: str                    # "bf16" or "f32"
+    scale_denominator: int        # scale = denominator ** -0.5
+    causal: bool = False
+    ragged: bool = False          # seqlens uniform in [1, context]
+    sigma: float = 0.5            # Q, KV ~ N(0, 1) * sigma
+    dense: bool = False           # identity block table over a dense cache
+    peak_rows: int = 0            # rows per sequence multiplied by peak_factor
+    peak_factor: float = 8.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> np.float32:
+        return np.float32(float(self.scale_denominator) ** -0.5)
+
+
+# The five workloads the method is exercised on, plus the 8K gate shape.
+WORKLOADS = {
+    "tiny_fp32_dense": Workload("tiny_fp32_dense", 1, 1, 16, 256, "f32", 576,
+                                sigma=1.0, dense=True, seed=0),
+    "paged_b16_l4096": Workload("paged_b16_l4096", 16, 1, 128, 4096, "bf16", 192, seed=1),
+    "ragged_b64_l8192": Workload("ragged_b64_l8192", 64, 1, 128, 8192, "bf16", 192,
+                                 ragged=True, seed=2),
+    "spec_b128_sq2_l16384": Workload("spec_b128_sq2_l16384", 128, 2, 128, 16384, "bf16", 192,
+                                     causal=True, seed=3),
+    "long_b4_l131072": Workload("long_b4_l131072", 4, 1, 128, 131072, "bf16", 192,
+                                peak_rows=4, seed=4),
+    "gate_b64_l8192": Workload("gate_b64_l8192", 64, 1, 128, 8192, "bf16", 192, seed=5),
+}
+
+
+def float32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); returns uint16 bits.
+
+    Finite inputs only (the generators never produce inf/nan before rounding).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_float32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits to float32 (for test helpers and fixtures)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _normal_fill(seed_seq: np.random.SeedSequence, n: int, sigma: float, bf16: bool) -> np.ndarray:
+    """n draws of N(0,1)*sigma in fixed chunks (thread-count independent)."""
+    nch = (n + _CHUNK - 1) // _CHUNK
+    kids = seed_seq.spawn(nch)
+    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
+    sig = np.float32(sigma)
+
+    def fill(i: int) -> None:
+        g = np.random.Generator(np.random.PCG64(kids[i]))
+        m = min(_CHUNK, n - i * _CHUNK)
+        x = g.standard_normal(m, dtype=np.float32)
+        if sigma != 1.0:
+            x *= sig
+        out[i * _CHUNK:i * _CHUNK + m] = float32_to_bf16_bits(x) if bf16 else x
+
+    if nch == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nch)))
+    return out
+
+
+def make_seqlens(w: Workload, rng: np.random.Generator) -> np.ndarray:
+    if w.ragged:
+        return rng.integers(1, w.context, size=w.batch, endpoint=True).astype(np.int32)
+    return np.full(w.batch, w.context, dtype=np.int32)
+
+
+def make_workload(w: Workload, seqlens: Optional[np.ndarray] = None, guard_blocks: int = 0,
+                  poison: bool = False) -> dict:
+    """Draw one workload.
+
+    ``seqlens`` overrides the drawn lengths (edge-case tests).  ``guard_blocks``
+    appends pool blocks that no sequence owns; with ``poison`` they, and every
+    row at or past a sequence's length inside its last block, are set to NaN
+    (a correct kernel never lets them reach the output).
+    """
+    streams = np.random.SeedSequence(w.seed).spawn(5)
+    rng_len = np.random.Generator(np.random.PCG64(streams[0]))
+    rng_perm = np.random.Generator(np.random.PCG64(streams[1]))
+    rng_peak = np.random.Generator(np.random.PCG64(streams[4]))
+
+    lens = make_seqlens(w, rng_len)
+    if seqlens is not None:
+        lens = np.asarray(seqlens, dtype=np.int32).copy()
+    B = int(lens.shape[0])
+    nblk = (lens.astype(np.int64) + PAGE - 1) // PAGE
+    total = int(nblk.sum())
+    max_blocks = max(1, int(nblk.max()) if B else 1)
+    num_blocks = total + guard_blocks
+
+    if w.dense:
+        perm = np.arange(num_blocks, dtype=np.int32)
+    else:
+        perm = rng_perm.permutation(num_blocks).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        k = int(nblk[b])
+        table[b, :k] = perm[off:off + k]
+        off += k
+
+    bf16 = w.dtype == "bf16"
+    q = _normal_fill(streams[2], B * w.s_q * w.heads * D_QK, w.sigma, bf16)
+    q = q.reshape(B, w.s_q, w.heads, D_QK)
+    kv = _normal_fill(streams[3], num_blocks * PAGE * D_QK, w.sigma, bf16)
+    kv = kv.reshape(max(num_blocks, 0), PAGE, D_QK)
+
+    peaks = []
+    if w.peak_rows:
+        for b in range(B):
+            L = int(lens[b])
+            k = min(w.peak_rows, L)
+            pos = np.sort(rng_peak.choice(L, size=k, replace=False)) if k else np.zeros(0, np.int64)
+            for p in pos:
+                blk, row = int(table[b, p // PAGE]), int(p % PAGE)
+                if bf16:
+                    vals = bf16_bits_to_float32(kv[blk, row]) * np.float32(w.peak_factor)
+                    kv[blk, row] = float32_to_bf16_bits(vals)
+                else:
+                    kv[blk, row] *= np.float32(w.peak_factor)
+                peaks.append((b, int(p)))
+
+    if poison:
+        nan = np.uint16(0x7FC0) if bf16 else np.float32(np.nan)
+        for b in range(B):
+            L = int(lens[b])
+            k = int(nblk[b])
+            if k and L % PAGE:
+                kv[table[b, k - 1], L % PAGE:, :] = nan
+        if guard_blocks:
+            used = np.zeros(num_blocks, bool)
+            used[table[table >= 0]] = True
+            kv[~used] = nan
+
+    return {
+        "workload": w,
+        "q": q,
+        "kv_cache": kv,
+        "block_table": table,
+        "seqlens": lens,
+        "scale": w.scale,
+        "causal": w.causal,
+        "peaks": peaks,
+    }
+
+
+def sample_sequences(batch: int, count: int, seed: int) -> np.ndarray:
+    """Indices of sequences checked one by one at full size: first, last and a seeded draw."""
+    rng = np.random.default_rng(seed + 1000)
+    pick = {0, batch - 1}
+    if batch > 2:
+        pick.update(int(i) for i in rng.choice(np.arange(1, batch - 1),
+                                                size=min(count, batch - 2), replace=False))
+    return np.array(sorted(pick), dtype=np.int64)

@@ -1,0 +1,9 @@
+"""CPU oracle for MLA decode attention (test infrastructure only).
+
+Imported by the tests, the smoke check and the bench's CPU-baseline leg, never
+by the product path.  It shares no code with the HIP kernels.
+"""
+from .mla_oracle import (  # noqa: F401
+    PAGE, D_QK, D_V, widen, visible_keys, gather_rows, check_lengths, attend_one,
+    mla_decode, softmax_weights, merge_partials, brute_force,
+)

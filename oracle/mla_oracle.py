@@ -1,0 +1,177 @@
+"""CPU oracle for MLA decode attention: test infrastructure, not the product.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg use this
+module.  It shares no code with the HIP path and imports nothing from it.
+
+What it computes is the plain definition of decode attention over a paged
+latent cache, as the DeepSeek-MLA / FlashMLA running example of the TileLang
+talk ("What is TileLang?", the DeepSeek MLA kernel and its layout-inference
+example) uses it, with the shapes of that example: each cache row holds 576
+values (512 latent + 64 rope), every head reads the same rows, K is the whole
+row and V is its first 512 values, the softmax is scaled, and the outputs are
+O and the natural-log log-sum-exp of the scaled scores.  The tile loop, online
+softmax and split/combine of the kernels are ways to reach exactly this
+result, so the oracle is the definition written out, in float64:
+
+    rows of sequence b:  R_b[j] = kv_cache[block_table[b, j // 64], j % 64, :]
+    visible keys of query token t:  n = L_b            (not causal)
+                                    n = L_b - s_q + 1 + t   (causal, the s_q
+                                    queries are the last s_q positions)
+    s_j        = scale * sum_d q[b,t,h,d] * R_b[j][d]          (j < n)
+    LSE[b,t,h] = ln sum_j exp(s_j)
+    O[b,t,h,c] = sum_j exp(s_j - LSE) * R_b[j][c]              (c < 512)
+
+A query with no visible key (n = 0) gets O = 0 and LSE = -inf.
+
+``merge_partials`` is the log-sum-exp merge of attention results over
+disjoint key sets; it is exercised against the unsplit definition.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Sequence, Tuple
+
+import numpy as np
+
+PAGE = 64
+D_QK = 576
+D_V = 512
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of an input array: bf16 bit patterns (uint16) or floats."""
+    if dtype == "bf16":
+        bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def visible_keys(seqlen: int, s_q: int, t: int, causal: bool) -> int:
+    """Number of keys query token t of a sequence may attend to."""
+    if not causal:
+        return seqlen
+    return seqlen - s_q + 1 + t
+
+
+def gather_rows(kv_cache: np.ndarray, block_table: np.ndarray, b: int, seqlen: int) -> np.ndarray:
+    """The first ``seqlen`` logical rows of sequence b, read through its block table."""
+    if seqlen == 0:
+        return kv_cache.reshape(-1, kv_cache.shape[-1])[:0]
+    nblk = (seqlen + PAGE - 1) // PAGE
+    blocks = np.asarray(block_table[b, :nblk], dtype=np.int64)
+    if (blocks < 0).any() or (blocks >= kv_cache.shape[0]).any():
+        raise ValueError(f"sequence {b}: block table entry outside the pool")
+    return kv_cache[blocks].reshape(nblk * PAGE, kv_cache.shape[-1])[:seqlen]
+
+
+def check_lengths(seqlens: np.ndarray, block_table: np.ndarray, s_q: int, causal: bool) -> None:
+    cap = block_table.shape[1] * PAGE
+    for b, L in enumerate(np.asarray(seqlens).tolist()):
+        if L < 0 or L > cap:
+            raise ValueError(f"sequence {b}: length {L} outside [0, {cap}]")
+        if causal and L < s_q:
+            raise ValueError(f"sequence {b}: causal length {L} shorter than {s_q} queries")
+
+
+def attend_one(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of query rows [H, 576] over keys [n, 576] (V = keys[:, :512]), float64.
+
+    Returns (O [H, 512], LSE [H]).  n = 0 gives O = 0 and LSE = -inf.
+    """
+    H = q_rows.shape[0]
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros((H, D_V)), np.full(H, -np.inf)
+    s = scale * (q_rows @ keys.T)                      # [H, n]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    tot = e.sum(axis=1, keepdims=True)
+    lse = (m + np.log(tot))[:, 0]
+    o = (e / tot) @ keys[:, :D_V]
+    return o, lse
+
+
+def mla_decode(q, kv_cache, block_table, seqlens, scale, causal=False, dtype="bf16",
+               batches: Iterable[int] | None = None):
+    """Float64 O [B, s_q, H, 512] and LSE [B, s_q, H] of MLA decode.
+
+    ``q``/``kv_cache`` hold bf16 bit patterns (dtype "bf16") or floats ("f32",
+    "f64").  ``scale`` is used as given (pass the float32 value the kernels see).
+    ``batches`` restricts the work to some sequences; the others stay NaN.
+    """
+    q = np.asarray(q)
+    B, s_q, H, D = q.shape
+    if D != D_QK or kv_cache.shape[1:] != (PAGE, D_QK):
+        raise ValueError("expected q [B,s_q,H,576] and kv_cache [blocks,64,576]")
+    seqlens = np.asarray(seqlens)
+    check_lengths(seqlens, block_table, s_q, causal)
+    scale = float(scale)
+    out = np.full((B, s_q, H, D_V), np.nan)
+    lse = np.full((B, s_q, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(seqlens[b])
+        keys = widen(gather_rows(kv_cache, block_table, b, L), dtype)
+        qb = widen(q[b], dtype)                          # [s_q, H, 576]
+        for t in range(s_q):
+            n = visible_keys(L, s_q, t, causal)
+            out[b, t], lse[b, t] = attend_one(qb[t], keys[:n], scale)
+    return out, lse
+
+
+def softmax_weights(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
+    """The attention weights p[h, j] = exp(s_j - LSE_h) the outputs are built from."""
+    s = scale * (q_rows @ keys.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):
+    """Merge attention results over disjoint key sets into the result over their union.
+
+    With LSE_i the log-sum-exp of part i, the union has LSE = ln sum_i exp(LSE_i)
+    and O = sum_i exp(LSE_i - LSE) * O_i.  Parts with no keys (LSE_i = -inf)
+    carry zero weight; if every part is empty the result is O = 0, LSE = -inf.
+    """
+    lse = np.stack([np.asarray(x, dtype=np.float64) for x in lses])        # [S, ...]
+    o = np.stack([np.asarray(x, dtype=np.float64) for x in outs])          # [S, ..., 512]
+    mx = lse.max(axis=0)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    w = np.where(np.isfinite(lse), np.exp(lse - safe), 0.0)
+    tot = w.sum(axis=0)
+    out_lse = np.where(tot > 0, safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    wn = np.where(tot > 0, w / np.where(tot > 0, tot, 1.0), 0.0)
+    return (wn[..., None] * o).sum(axis=0), out_lse
+
+
+def brute_force(q_list, keys_list, scale: float, causal: bool, s_q: int):
+    """Pure-Python loops over dense per-sequence keys, for tiny cases.
+
+    ``q_list[b][t][h]`` is a list of 576 floats; ``keys_list[b]`` a list of rows.
+    Sums use math.fsum, exponentials math.exp.  Returns nested lists
+    (O[b][t][h][c], LSE[b][t][h]).
+    """
+    outs, lses = [], []
+    for b, rows in enumerate(keys_list):
+        ob, lb = [], []
+        for t in range(s_q):
+            n = visible_keys(len(rows), s_q, t, causal)
+            ot, lt = [], []
+            for qh in q_list[b][t]:
+                if n == 0:
+                    ot.append([0.0] * D_V)
+                    lt.append(-math.inf)
+                    continue
+                s = [scale * math.fsum(qh[d] * rows[j][d] for d in range(D_QK)) for j in range(n)]
+                m = max(s)
+                z = math.fsum(math.exp(x - m) for x in s)
+                L = m + math.log(z)
+                p = [math.exp(x - L) for x in s]
+                ot.append([math.fsum(p[j] * rows[j][c] for j in range(n)) for c in range(D_V)])
+                lt.append(L)
+            ob.append(ot)
+            lb.append(lt)
+        outs.append(ob)
+        lses.append(lb)
+    return outs, lses

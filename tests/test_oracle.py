@@ -1,0 +1,289 @@
+"""Pins for the CPU oracle: checks against what the definition and mathematics fix.
+
+None of these compare the oracle with itself.  Each targets a plausible mistake:
+a wrong softmax normalisation or log base (closed forms, uniform scores), a
+wrong gather or block-table order (brute force on dense keys, hand-derived
+paged fixture, re-permuted pools), a wrong causal offset (hand-derived causal
+fixture, causal reduction), a transposed operand or index (equivariance,
+brute force), masking by multiplication (NaN tails), and a wrong merge rule
+(split/combine identity).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from mla_decode_attention_flashmla_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
+
+
+def _val(v):
+    if isinstance(v, (int, float)):
+        return float(v)
+    if v.startswith("ln"):
+        return math.log(float(v[2:]))
+    if "/" in v:
+        a, b = v.split("/")
+        return float(a) / float(b)
+    return float(v)
+
+
+def _load_case(c):
+    B, s_q, H = c["batch"], c["s_q"], c["heads"]
+    q = np.zeros((B, s_q, H, 576))
+    for b, t, h, d, v in c["q"]:
+        q[b, t, h, d] = _val(v)
+    kv = np.zeros((c["num_blocks"], 64, 576))
+    L = c["seqlens"]
+    for e in c["kv"]:
+        if e[0] == "rows_of_block":
+            _, blk, col, _ = e
+            kv[blk, :, col] = np.arange(64)
+        elif e[0] == "tail_of_block":
+            _, blk, col, v = e
+            kv[blk, L[0] % 64:, col] = _val(v)
+        else:
+            blk, row, col, v = e
+            kv[blk, row, col] = _val(v)
+    return q, kv, np.array(c["block_table"], np.int32), np.array(L, np.int32)
+
+
+def _cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: c["name"])
+def test_golden_closed_forms(case):
+    q, kv, table, lens = _load_case(case)
+    out, lse = O.mla_decode(q, kv, table, lens, case["scale"], case["causal"], dtype="f64")
+    exp_out = np.zeros_like(out)
+    for b, t, h, col, v in case["expect_out"]:
+        exp_out[b, t, h, col] = _val(v)
+    exp_lse = np.zeros_like(lse)
+    for b, t, h, v in case["expect_lse"]:
+        exp_lse[b, t, h] = _val(v)
+    np.testing.assert_allclose(out, exp_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, exp_lse, rtol=0, atol=1e-12)
+
+
+def _rand_case(rng, B, s_q, H, lens, causal=False, extra_blocks=0):
+    lens = np.asarray(lens, np.int32)
+    nblk = (lens + 63) // 64
+    total = int(nblk.sum()) + extra_blocks
+    perm = rng.permutation(total)
+    table = np.full((B, max(1, int(nblk.max()))), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    kv = rng.standard_normal((total, 64, 576))
+    q = rng.standard_normal((B, s_q, H, 576))
+    return q, kv, table, lens
+
+
+def _dense_keys(kv, table, lens):
+    """Dense per-sequence rows, built with explicit loops (independent of gather_rows)."""
+    out = []
+    for b, L in enumerate(lens.tolist()):
+        rows = []
+        for j in range(L):
+            rows.append([float(x) for x in kv[table[b][j // 64], j % 64]])
+        out.append(rows)
+    return out
+
+
+def test_single_token_returns_that_row():
+    """P1: one visible key -> weight 1: O is that V row exactly, LSE is its score."""
+    rng = np.random.default_rng(11)
+    q, kv, table, lens = _rand_case(rng, 2, 1, 4, [1, 1])
+    out, lse = O.mla_decode(q, kv, table, lens, 0.125, dtype="f64")
+    for b in range(2):
+        row = kv[table[b, 0], 0]
+        assert np.array_equal(out[b, 0], np.broadcast_to(row[:512], (4, 512)))
+        for h in range(4):
+            s0 = 0.125 * math.fsum(q[b, 0, h, d] * row[d] for d in range(576))
+            assert abs(lse[b, 0, h] - s0) < 1e-12
+
+
+def test_uniform_scores_give_mean_and_log_n():
+    """P2: q = 0 -> every score 0 -> LSE = ln n, O = arithmetic mean of the V rows."""
+    rng = np.random.default_rng(12)
+    q, kv, table, lens = _rand_case(rng, 2, 1, 3, [70, 5])
+    q[:] = 0.0
+    out, lse = O.mla_decode(q, kv, table, lens, 0.3, dtype="f64")
+    for b, L in enumerate(lens.tolist()):
+        rows = [kv[table[b, j // 64], j % 64] for j in range(L)]
+        mean = np.array([math.fsum(r[c] for r in rows) / L for c in range(512)])
+        np.testing.assert_allclose(out[b, 0], np.broadcast_to(mean, (3, 512)), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[b, 0], math.log(L), rtol=0, atol=1e-14)
+
+
+def test_identical_keys_distinct_values():
+    """P2': scores equal because the query only reads rope columns that are equal across rows,
+    while the latent (V) columns differ: O = mean of V, LSE = s + ln n."""
+    rng = np.random.default_rng(13)
+    q, kv, table, lens = _rand_case(rng, 1, 1, 2, [100])
+    q[..., :512] = 0.0
+    rope = rng.standard_normal(64)
+    kv[:, :, 512:] = rope
+    scale = 0.07
+    out, lse = O.mla_decode(q, kv, table, lens, scale, dtype="f64")
+    rows = [kv[table[0, j // 64], j % 64] for j in range(100)]
+    mean = np.array([math.fsum(r[c] for r in rows) / 100 for c in range(512)])
+    for h in range(2):
+        s = scale * math.fsum(q[0, 0, h, 512 + d] * rope[d] for d in range(64))
+        np.testing.assert_allclose(out[0, 0, h], mean, rtol=0, atol=1e-13)
+        assert abs(lse[0, 0, h] - (s + math.log(100))) < 1e-12
+
+
+def test_weights_sum_to_one_and_lse_closed_form():
+    """P3 + P4: sum of weights is 1; LSE equals ln(fsum(exp(s))) without max shift."""
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((5, 576))
+    keys = rng.standard_normal((300, 576))
+    scale = 576 ** -0.5
+    p = O.softmax_weights(q, keys, scale)
+    assert np.all(np.abs(p.sum(axis=1) - 1.0) < 1e-14)
+    _, lse = O.attend_one(q, keys, scale)
+    for h in range(5):
+        s = [scale * math.fsum(q[h, d] * keys[j, d] for d in range(576)) for j in range(300)]
+        assert abs(lse[h] - math.log(math.fsum(math.exp(x) for x in s))) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(causal):
+    """P5: pure-Python loops (fsum, math.exp) over dense keys agree to 1e-12."""
+    rng = np.random.default_rng(15 + causal)
+    lens = [6, 3] if causal else [6, 1]
+    q, kv, table, lens = _rand_case(rng, 2, 2, 3, lens, causal=causal, extra_blocks=1)
+    scale = 0.2
+    out, lse = O.mla_decode(q, kv, table, lens, scale, causal, dtype="f64")
+    qb = [[[list(map(float, q[b, t, h])) for h in range(3)] for t in range(2)] for b in range(2)]
+    bo, bl = O.brute_force(qb, _dense_keys(kv, table, lens), scale, causal, 2)
+    np.testing.assert_allclose(out, np.array(bo), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(bl), rtol=0, atol=1e-12)
+
+
+def test_paging_invariance():
+    """P6: moving blocks to other pool slots (and rewriting the table) changes nothing."""
+    rng = np.random.default_rng(16)
+    q, kv, table, lens = _rand_case(rng, 3, 1, 4, [130, 64, 1], extra_blocks=2)
+    out1, lse1 = O.mla_decode(q, kv, table, lens, 0.1, dtype="f64")
+    p = rng.permutation(kv.shape[0])
+    kv2 = np.empty_like(kv)
+    kv2[p] = kv
+    table2 = np.where(table >= 0, p[np.maximum(table, 0)], -1).astype(np.int32)
+    out2, lse2 = O.mla_decode(q, kv2, table2, lens, 0.1, dtype="f64")
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_split_combine_identity():
+    """P7: attending over disjoint key chunks and merging by LSE equals the unsplit result,
+    with empty chunks carrying zero weight."""
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((4, 576))
+    keys = rng.standard_normal((500, 576)) * 2.0
+    scale = 0.09
+    o_ref, l_ref = O.attend_one(q, keys, scale)
+    cuts = [0, 0, 17, 64, 64, 300, 499, 500, 500]
+    parts = [O.attend_one(q, keys[a:b], scale) for a, b in zip(cuts[:-1], cuts[1:])]
+    o, l = O.merge_partials([x[0] for x in parts], [x[1] for x in parts])
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-13)
+    # all parts empty
+    o0, l0 = O.merge_partials([np.zeros((4, 512))] * 2, [np.full(4, -np.inf)] * 2)
+    assert np.all(o0 == 0) and np.all(np.isneginf(l0))
+
+
+def test_causal_reduction():
+    """P8: with 2 causal queries, token 1 equals the 1-query result at length L and
+    token 0 equals the 1-query result at length L-1."""
+    rng = np.random.default_rng(18)
+    q, kv, table, lens = _rand_case(rng, 2, 2, 3, [129, 2], causal=True)
+    out, lse = O.mla_decode(q, kv, table, lens, 0.1, True, dtype="f64")
+    o1, l1 = O.mla_decode(q[:, 1:2], kv, table, lens, 0.1, False, dtype="f64")
+    o0, l0 = O.mla_decode(q[:, 0:1], kv, table, lens - 1, 0.1, False, dtype="f64")
+    np.testing.assert_array_equal(out[:, 1], o1[:, 0])
+    np.testing.assert_array_equal(lse[:, 1], l1[:, 0])
+    np.testing.assert_array_equal(out[:, 0], o0[:, 0])
+    np.testing.assert_array_equal(lse[:, 0], l0[:, 0])
+
+
+def test_equivariance_heads_and_sequences():
+    """P9: permuting heads or sequences permutes the outputs the same way."""
+    rng = np.random.default_rng(19)
+    q, kv, table, lens = _rand_case(rng, 3, 1, 5, [10, 70, 3])
+    out, lse = O.mla_decode(q, kv, table, lens, 0.1, dtype="f64")
+    ph = rng.permutation(5)
+    o2, l2 = O.mla_decode(q[:, :, ph], kv, table, lens, 0.1, dtype="f64")
+    np.testing.assert_allclose(o2, out[:, :, ph], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l2, lse[:, :, ph], rtol=0, atol=1e-14)
+    pb = np.array([2, 0, 1])
+    o3, l3 = O.mla_decode(q[pb], kv, table[pb], lens[pb], 0.1, dtype="f64")
+    np.testing.assert_allclose(o3, out[pb], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l3, lse[pb], rtol=0, atol=1e-14)
+
+
+def test_nan_tail_and_guard_blocks_do_not_leak():
+    """P10: NaN rows past each length and NaN unowned blocks leave the result finite and unchanged."""
+    w = I.Workload("t", 3, 1, 4, 200, "bf16", 192, ragged=True, seed=21)
+    clean = I.make_workload(w, seqlens=[200, 65, 7], guard_blocks=2)
+    dirty = I.make_workload(w, seqlens=[200, 65, 7], guard_blocks=2, poison=True)
+    assert np.isnan(O.widen(dirty["kv_cache"], "bf16")).any()
+    a = O.mla_decode(clean["q"], clean["kv_cache"], clean["block_table"], clean["seqlens"], w.scale)
+    b = O.mla_decode(dirty["q"], dirty["kv_cache"], dirty["block_table"], dirty["seqlens"], w.scale)
+    assert np.isfinite(b[0]).all() and np.isfinite(b[1]).all()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_sharp_peaks_stay_finite_and_dominate():
+    """P11: rows scaled x8 produce large scores; LSE stays finite and a peak row that
+    holds the largest score carries the largest weight."""
+    w = I.Workload("t", 1, 1, 8, 3000, "bf16", 192, peak_rows=4, seed=22)
+    d = I.make_workload(w)
+    out, lse = O.mla_decode(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], w.scale)
+    assert np.isfinite(lse).all() and np.isfinite(out).all()
+    keys = O.widen(O.gather_rows(d["kv_cache"], d["block_table"], 0, 3000), "bf16")
+    qr = O.widen(d["q"][0, 0], "bf16")
+    p = O.softmax_weights(qr, keys, float(w.scale))
+    peak_pos = {pos for _, pos in d["peaks"]}
+    s = float(w.scale) * (qr @ keys.T)
+    for h in range(8):
+        if int(np.argmax(s[h])) in peak_pos:
+            assert int(np.argmax(p[h])) in peak_pos
+    assert any(int(np.argmax(s[h])) in peak_pos for h in range(8))
+
+
+def test_empty_sequence_convention():
+    """A sequence of length 0 has no visible key: O = 0, LSE = -inf."""
+    rng = np.random.default_rng(23)
+    q, kv, table, lens = _rand_case(rng, 2, 1, 2, [0, 5])
+    out, lse = O.mla_decode(q, kv, table, lens, 0.1, dtype="f64")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.isfinite(lse[1]).all()
+
+
+def test_invalid_lengths_rejected():
+    rng = np.random.default_rng(24)
+    q, kv, table, lens = _rand_case(rng, 1, 2, 1, [5])
+    with pytest.raises(ValueError):
+        O.mla_decode(q, kv, table, np.array([65], np.int32), 0.1, dtype="f64")
+    with pytest.raises(ValueError):
+        O.mla_decode(q, kv, table, np.array([-1], np.int32), 0.1, dtype="f64")
+    with pytest.raises(ValueError):
+        O.mla_decode(q, kv, table, np.array([1], np.int32), 0.1, causal=True, dtype="f64")
+
+
+def test_bf16_widening_is_exact():
+    """The oracle reads the exact bf16 values: a few hand-checked bit patterns."""
+    bits = np.array([0x3F80, 0xC000, 0x3EAB, 0x0000, 0x7F7F], np.uint16)
+    vals = O.widen(bits, "bf16")
+    assert vals[0] == 1.0 and vals[1] == -2.0 and vals[3] == 0.0
+    assert vals[2] == 0.333984375           # 0x3EAB = 1.0101011b * 2^-2
+    assert vals[4] == 3.3895313892515355e38  # largest finite bf16
