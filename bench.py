@@ -1,0 +1,240 @@
+"""Throughput of MLA decode on one MI355X, as a fraction of the HBM/MFMA roofline.
+
+One step = the whole hot path on one batch: split metadata (scheduler kernel),
+main kernel, log-sum-exp combine, on inputs already resident in HBM.  Prints one
+JSON line.  The default workload is the 64 x 8K-context, 128-head bf16 paged
+decode; --workload selects another seeded one.
+
+Algorithmic work per step (each KV row read once, shared by every head):
+  bytes = sum_b L_b*576*e + B*s_q*H*(576*e + 512*4 + 4) + sum_b nblk_b*4 + B*4
+  flops = 2*H*(576+512)*sum_{b,t} n_{b,t}
+roofline time = max(bytes / 8.0 TB/s, flops / 2516.6 TFLOP/s (bf16 dense MFMA)).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2516.6e12, "f32": 157.3e12}   # dense flop/s
+METRIC = "MLA decode TFLOP/s + KV-read GB/s (H=128, bf16, paged) as % of roofline"
+KERNEL_SRC = os.path.join(ROOT, "mla_decode_attention_flashmla_amd", "csrc", "mla_main_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_main_bf16_kernel_traffic.json")
+
+
+def algorithmic_work(d):
+    import numpy as np
+
+    w = d["workload"]
+    e = 2 if w.dtype == "bf16" else 4
+    lens = d["seqlens"].astype(np.int64)
+    B, s_q, H = w.batch, w.s_q, w.heads
+    kv = int(lens.sum()) * 576 * e
+    nblk = int(((lens + 63) // 64).sum())
+    byt = kv + B * s_q * H * (576 * e + 512 * 4 + 4) + nblk * 4 + B * 4
+    vis = 0
+    for L in lens.tolist():
+        for t in range(s_q):
+            vis += (L - s_q + 1 + t) if w.causal else L
+    flops = 2 * H * (576 + 512) * vis
+    return byt, kv, flops
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in ("mla_main_bf16.hip", "mla_internal.h", "mla_oacc_asm.h"):
+        with open(os.path.join(os.path.dirname(KERNEL_SRC), f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on this exact kernel source and workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(d, budget_s: float):
+    """Time the CPU oracle on whole sequences of the same workload until budget_s is spent."""
+    import numpy as np
+    from oracle import mla_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    w = d["workload"]
+    done = []
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        O.mla_decode(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], d["scale"],
+                     d["causal"], dtype=w.dtype, batches=[b])
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    frac = float(d["seqlens"][done].astype(np.int64).sum()) / float(d["seqlens"].astype(np.int64).sum())
+    return el, frac, len(done), cores
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gate_b64_l8192")
+    ap.add_argument("--num-workgroups", type=int, default=0)
+    ap.add_argument("--min-split-blocks", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, copy this many MiB once (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode runs on a single GPU, with no inter-GPU sharding).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_flashmla_amd import binding as B
+    from mla_decode_attention_flashmla_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = I.make_workload(w)
+    dev = torch.device("cuda", 0)
+    if w.dtype == "bf16":
+        q = torch.from_numpy(d["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+        kv = torch.from_numpy(d["kv_cache"].view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        q = torch.from_numpy(d["q"]).to(dev)
+        kv = torch.from_numpy(d["kv_cache"]).to(dev)
+    table = torch.from_numpy(d["block_table"]).to(dev)
+    lens = torch.from_numpy(d["seqlens"]).to(dev)
+    Bn, s_q, H = w.batch, w.s_q, w.heads
+    out = torch.empty((Bn, s_q, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((Bn, s_q, H), dtype=torch.float32, device=dev)
+    nwg = args.num_workgroups or B.device_workgroups(0)
+    plan = B.alloc_plan(Bn, s_q, H, w.causal, table.shape[1], nwg, dev)
+    scale = float(d["scale"])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        B.get_split_metadata(lens, plan, args.min_split_blocks)
+        if ev is not None:
+            ev[0].record(stream)
+        B.decode_main(q, kv, table, lens, scale, out, lse, plan)
+        if ev is not None:
+            ev[1].record(stream)
+        B.decode_combine(q, kv, table, lens, scale, out, lse, plan)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if B.read_status(plan) != 0:
+        raise SystemExit("device status flagged an error")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    main_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    ms_step = total_ms / args.steps
+    main_avg_us = float(np.mean(main_us))
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    byt, kv_bytes, flops = algorithmic_work(d)
+    t_roof = max(byt / HBM_PEAK, flops / MFMA_PEAK[w.dtype])
+    bound = "hbm" if byt / HBM_PEAK >= flops / MFMA_PEAK[w.dtype] else "mfma"
+    step_s = ms_step * 1e-3
+    main_s = main_avg_us * 1e-6
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": byt / main_s / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / main_s / 1e12,
+                "peak": MFMA_PEAK[w.dtype] / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = "mla_main_bf16_kernel" if w.dtype == "bf16" else "mla_main_f32_kernel"
+    roof["kernel_us"] = main_avg_us
+
+    res = {
+        "metric": METRIC,
+        "value": 100.0 * t_roof / step_s,
+        "unit": "% of roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": Bn, "s_q": s_q, "heads": H,
+                   "seq_len": w.context, "ragged": w.ragged, "causal": w.causal,
+                   "block_size": 64, "head_dim": 576, "v_dim": 512,
+                   "num_workgroups": nwg, "parallelism": "single-gpu"},
+        "tflops": flops / step_s / 1e12,
+        "kv_gbs": kv_bytes / step_s / 1e9,
+        "alg_bytes": byt,
+        "alg_flops": flops,
+        "roofline_us": t_roof * 1e6,
+        "wall_s": wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline (budget {args.cpu_budget}s)", file=sys.stderr,
+              flush=True)
+        el, frac, nseq, cores = cpu_baseline(d, args.cpu_budget)
+        t_full = el / frac
+        res["cpu_baseline"] = {
+            "value": 100.0 * t_roof / t_full, "unit": "% of roofline",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{nseq} of {Bn} sequences ({frac * 100:.1f}% of the keys), fp64 numpy, "
+                      f"{el:.1f} s; scaled to the whole batch",
+            "seconds_per_step_est": t_full,
+            "tflops": flops / t_full / 1e12,
+        }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

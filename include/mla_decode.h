@@ -1,0 +1,160 @@
+/*
+ * MLA decode attention on MI355X (gfx950): C ABI of libmla_decode.so.
+ *
+ * What it computes.  The DeepSeek-MLA decode step that the TileLang talk uses
+ * as its running example (section "What is TileLang?": the DeepSeek MLA
+ * kernel, its tile configuration, and the layout-inference example in which
+ * the score accumulator is reduced to the per-row maximum).  For every
+ * sequence b, query token t (0 <= t < s_q) and head h:
+ *
+ *   R_b[j]  = kv_cache[block_table[b][j / 64]][j % 64][0..575]   (j < L_b)
+ *   n       = L_b, or L_b - s_q + 1 + t with the causal mask (the s_q queries
+ *             are the last s_q positions of the sequence)
+ *   s_j     = scale * sum_d q[b][t][h][d] * R_b[j][d]             (j < n)
+ *   lse     = ln sum_j exp(s_j)                 (natural log, scaled scores)
+ *   out[c]  = sum_j exp(s_j - lse) * R_b[j][c]                    (c < 512)
+ *
+ * All heads read the same 576-wide latent rows (512 latent + 64 rope); V is
+ * the first 512 values of each row.  A query with no visible key gets
+ * out = 0 and lse = -inf.
+ *
+ * Memory.  Every pointer argument below is a DEVICE pointer except `status`
+ * (host) in mla_read_status.  The caller owns all buffers; the library never
+ * allocates device memory and keeps no per-call state.  Inputs are never
+ * modified.  All tensors are dense and row-major:
+ *
+ *   q            [batch][s_q][num_heads][576]        dtype (16-byte aligned)
+ *   kv_cache     [num_blocks][64][576]               dtype (16-byte aligned)
+ *   block_table  [batch][max_blocks_per_seq]         int32; entries past
+ *                ceil(L_b / 64) are never read
+ *   seqlens      [batch]                             int32
+ *   out          [batch][s_q][num_heads][512]        float32 (16-byte aligned)
+ *   lse          [batch][s_q][num_heads]             float32
+ *
+ * Streams.  Calls only enqueue work on `stream` (a hipStream_t; NULL is the
+ * null stream) and return; none synchronizes except mla_read_status.
+ *
+ * Errors.  Every entry point returns MLA_OK (0) or a negative MLA_ERR_* code.
+ * Arguments are validated on the host before any HIP call; on error nothing
+ * is enqueued.  Problems only the device can see (bad lengths or block
+ * numbers, a plan built for other lengths) set bits in the plan's status word
+ * (MLA_STATUS_*) and turn the affected sequences' out/lse into NaN; read it
+ * with mla_read_status.  Nothing throws or aborts across this boundary.
+ * Calls on distinct plans/workspaces may run concurrently.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_PAGE_SIZE 64
+#define MLA_HEAD_DIM 576
+#define MLA_V_DIM 512
+
+/* Return codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, misalignment, non-finite scale */
+#define MLA_ERR_UNSUPPORTED (-2) /* unknown dtype, s_q * num_heads above MLA_MAX_ROWS */
+#define MLA_ERR_PLAN (-3)        /* metadata or workspace buffer too small for these sizes */
+#define MLA_ERR_HIP (-4)         /* a HIP runtime call failed (launch, copy, device query) */
+
+/* Element types of q and kv_cache (out/lse are always float32). */
+#define MLA_DTYPE_F32 0
+#define MLA_DTYPE_BF16 1
+
+/* Largest s_q * num_heads per call. */
+#define MLA_MAX_ROWS 1024
+
+/* Device status bits (mla_read_status). */
+#define MLA_STATUS_BAD_SEQLEN 1     /* L_b < 0, L_b > 64 * max_blocks_per_seq, or causal L_b < s_q */
+#define MLA_STATUS_BAD_BLOCK 2      /* a block_table entry read was outside [0, num_blocks) */
+#define MLA_STATUS_PLAN_MISMATCH 4  /* plan built for other sizes or other seqlens */
+
+/*
+ * Number of workgroups to plan for on `device`: its compute-unit count.
+ * One HIP call (device attribute query).  Returns MLA_ERR_HIP without a GPU.
+ */
+int mla_device_workgroups(int device, int* num_workgroups);
+
+/*
+ * Host-only, pure: bytes of the scheduling metadata (`meta`) and of the split
+ * workspace that mla_get_split_metadata / mla_decode_fwd need for these sizes.
+ * num_workgroups: the persistent grid size (typically mla_device_workgroups).
+ */
+int mla_plan_size(int batch, int s_q, int num_heads, int num_workgroups,
+                  size_t* meta_bytes, size_t* workspace_bytes);
+
+/*
+ * Split-KV tile scheduler (one small kernel).  Reads seqlens on the device and
+ * writes the work partition into `meta` (device, >= meta_bytes from
+ * mla_plan_size): the concatenated stream of 64-token blocks of every
+ * (sequence, 128-row group) is cut into near-equal contiguous ranges, one per
+ * workgroup; a sequence cut at a range boundary is computed in parts and
+ * merged by log-sum-exp.  min_split_blocks (0 = library default of 8) is the
+ * smallest range a workgroup is given, which bounds the number of parts.
+ * The plan is reusable by every mla_decode_fwd with the same sizes and
+ * seqlens (e.g. all layers of one decode step).
+ */
+int mla_get_split_metadata(const int32_t* seqlens, int batch, int s_q, int num_heads,
+                           int causal, int max_blocks_per_seq, int num_workgroups,
+                           int min_split_blocks, int32_t* meta, size_t meta_bytes,
+                           void* stream);
+
+/*
+ * MLA decode forward: enqueues the main kernel (paged gather into LDS, scores
+ * and PV on MFMA, online softmax) and the log-sum-exp combine of split parts.
+ * meta/num_workgroups: from mla_get_split_metadata with the same sizes.
+ * workspace: device scratch of >= workspace_bytes (mla_plan_size) for the
+ * partial results of split sequences; no zeroing needed.
+ * dtype: MLA_DTYPE_BF16 (MFMA path) or MLA_DTYPE_F32 (fp32 path).
+ */
+int mla_decode_fwd(int dtype, const void* q, const void* kv_cache, int64_t num_blocks,
+                   const int32_t* block_table, int max_blocks_per_seq,
+                   const int32_t* seqlens, int batch, int s_q, int num_heads, int causal,
+                   float scale, float* out, float* lse,
+                   int32_t* meta, size_t meta_bytes, int num_workgroups,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of mla_decode_fwd, for callers that time or schedule them
+ * apart (same arguments and rules as mla_decode_fwd):
+ *   mla_decode_main     the main kernel: every segment computed whole writes
+ *                       out/lse; split segments write their parts to workspace;
+ *   mla_decode_combine  the log-sum-exp merge of those parts into out/lse, and
+ *                       out = 0 / lse = -inf (NaN for invalid lengths) for
+ *                       sequences with no key.
+ * mla_decode_main followed by mla_decode_combine on one stream equals
+ * mla_decode_fwd.
+ */
+int mla_decode_main(int dtype, const void* q, const void* kv_cache, int64_t num_blocks,
+                    const int32_t* block_table, int max_blocks_per_seq,
+                    const int32_t* seqlens, int batch, int s_q, int num_heads, int causal,
+                    float scale, float* out, float* lse,
+                    int32_t* meta, size_t meta_bytes, int num_workgroups,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int mla_decode_combine(int dtype, const void* q, const void* kv_cache, int64_t num_blocks,
+                       const int32_t* block_table, int max_blocks_per_seq,
+                       const int32_t* seqlens, int batch, int s_q, int num_heads, int causal,
+                       float scale, float* out, float* lse,
+                       int32_t* meta, size_t meta_bytes, int num_workgroups,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronizes `stream`, then copies the plan's device status word
+ * (MLA_STATUS_* bits, 0 = clean) into *status (host pointer).
+ */
+int mla_read_status(const int32_t* meta, void* stream, int32_t* status);
+
+/* Static, human-readable text of an MLA_* return code. */
+const char* mla_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,200 @@
+"""Thin ctypes binding over libmla_decode.so (same names as the C ABI).
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels.  PyTorch supplies device memory (``tensor.data_ptr()``) and the current
+stream; nothing here computes attention.  If the library is missing, every call
+raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla_decode.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_PLAN = -3
+MLA_ERR_HIP = -4
+MLA_DTYPE_F32 = 0
+MLA_DTYPE_BF16 = 1
+MLA_STATUS_BAD_SEQLEN = 1
+MLA_STATUS_BAD_BLOCK = 2
+MLA_STATUS_PLAN_MISMATCH = 4
+PAGE = 64
+D_QK = 576
+D_V = 512
+
+EXPORTS = ("mla_device_workgroups", "mla_plan_size", "mla_get_split_metadata",
+           "mla_decode_fwd", "mla_decode_main", "mla_decode_combine", "mla_read_status",
+           "mla_status_string")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {status_string(code)} ({code})")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load libmla_decode.so from the package directory (built by build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m mla_decode_attention_flashmla_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_i64, c_sz, c_p, c_f = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                                    ctypes.c_void_p, ctypes.c_float)
+    lib.mla_device_workgroups.argtypes = [c_int, ctypes.POINTER(c_int)]
+    lib.mla_plan_size.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(c_sz),
+                                  ctypes.POINTER(c_sz)]
+    lib.mla_get_split_metadata.argtypes = [c_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                           c_p, c_sz, c_p]
+    fwd_args = [c_int, c_p, c_p, c_i64, c_p, c_int, c_p, c_int, c_int, c_int, c_int, c_f, c_p,
+                c_p, c_p, c_sz, c_int, c_p, c_sz, c_p]
+    for fn in ("mla_decode_fwd", "mla_decode_main", "mla_decode_combine"):
+        getattr(lib, fn).argtypes = fwd_args
+    lib.mla_read_status.argtypes = [c_p, c_p, ctypes.POINTER(ctypes.c_int32)]
+    lib.mla_status_string.argtypes = [c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    for fn in EXPORTS:
+        if fn != "mla_status_string":
+            getattr(lib, fn).restype = c_int
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().mla_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != MLA_OK:
+        raise MlaError(fn, code)
+
+
+def device_workgroups(device: int = 0) -> int:
+    n = ctypes.c_int(0)
+    _check("mla_device_workgroups", load().mla_device_workgroups(device, ctypes.byref(n)))
+    return n.value
+
+
+def plan_size(batch: int, s_q: int, heads: int, num_workgroups: int) -> tuple[int, int]:
+    m, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mla_plan_size", load().mla_plan_size(batch, s_q, heads, num_workgroups,
+                                                 ctypes.byref(m), ctypes.byref(w)))
+    return m.value, w.value
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class Plan:
+    """Device buffers of one split plan: metadata (int32) and partial workspace (bytes)."""
+    meta: "object"
+    workspace: "object"
+    batch: int
+    s_q: int
+    heads: int
+    causal: int
+    max_blocks: int
+    num_workgroups: int
+
+
+def alloc_plan(batch: int, s_q: int, heads: int, causal: bool, max_blocks: int,
+               num_workgroups: Optional[int] = None, device=None) -> Plan:
+    """Allocate (with torch) the metadata and workspace buffers a plan needs."""
+    import torch
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    if num_workgroups is None:
+        num_workgroups = device_workgroups(device.index or 0)
+    mb, wb = plan_size(batch, s_q, heads, num_workgroups)
+    meta = torch.empty(mb // 4, dtype=torch.int32, device=device)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=device)
+    return Plan(meta, ws, batch, s_q, heads, int(bool(causal)), max_blocks, num_workgroups)
+
+
+def get_split_metadata(seqlens, plan: Plan, min_split_blocks: int = 0, stream=None) -> None:
+    """mla_get_split_metadata: fill plan.meta from seqlens (int32 device tensor)."""
+    _check("mla_get_split_metadata", load().mla_get_split_metadata(
+        seqlens.data_ptr(), plan.batch, plan.s_q, plan.heads, plan.causal, plan.max_blocks,
+        plan.num_workgroups, min_split_blocks, plan.meta.data_ptr(),
+        plan.meta.numel() * 4, _stream(stream)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MLA_DTYPE_F32
+    raise MlaError("dtype", MLA_ERR_UNSUPPORTED)
+
+
+def _decode(fn: str, q, kv_cache, block_table, seqlens, scale: float, out, lse, plan: Plan,
+            stream=None) -> None:
+    lib = load()
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seqlens", seqlens), ("out", out), ("lse", lse)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, s_q, H, D = q.shape
+    if (D != D_QK or kv_cache.shape[1:] != (PAGE, D_QK) or block_table.shape[0] != B
+            or tuple(out.shape) != (B, s_q, H, D_V) or tuple(lse.shape) != (B, s_q, H)
+            or kv_cache.dtype != q.dtype):
+        raise ValueError("shape/dtype mismatch with q [B,s_q,H,576], kv [n,64,576]")
+    _check(fn, getattr(lib, fn)(
+        _dtype_code(q), q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
+        block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), B, s_q, H,
+        plan.causal, float(scale), out.data_ptr(), lse.data_ptr(), plan.meta.data_ptr(),
+        plan.meta.numel() * 4, plan.num_workgroups, plan.workspace.data_ptr(),
+        plan.workspace.numel(), _stream(stream)))
+
+
+def decode_fwd(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream=None):
+    """mla_decode_fwd: main kernel + LSE combine into out [B,s_q,H,512] and lse [B,s_q,H]."""
+    _decode("mla_decode_fwd", q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream)
+
+
+def decode_main(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream=None):
+    _decode("mla_decode_main", q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream)
+
+
+def decode_combine(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream=None):
+    _decode("mla_decode_combine", q, kv_cache, block_table, seqlens, scale, out, lse, plan,
+            stream)
+
+
+def read_status(plan: Plan, stream=None) -> int:
+    v = ctypes.c_int32(0)
+    _check("mla_read_status", load().mla_read_status(plan.meta.data_ptr(), _stream(stream),
+                                                     ctypes.byref(v)))
+    return v.value
+
+
+def mla_decode(q, kv_cache, block_table, seqlens, scale, causal=False, plan=None,
+               min_split_blocks: int = 0, num_workgroups: Optional[int] = None):
+    """Convenience: plan + forward.  Returns (out, lse) float32 tensors."""
+    import torch
+    B, s_q, H, _ = q.shape
+    if plan is None:
+        plan = alloc_plan(B, s_q, H, causal, block_table.shape[1], num_workgroups, q.device)
+        get_split_metadata(seqlens, plan, min_split_blocks)
+    out = torch.empty((B, s_q, H, D_V), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q.device)
+    decode_fwd(q, kv_cache, block_table, seqlens, scale, out, lse, plan)
+    return out, lse

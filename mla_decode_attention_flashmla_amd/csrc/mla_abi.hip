@@ -1,0 +1,168 @@
+// C ABI of libmla_decode.so: host-side validation, plan sizing and launches.
+//
+// Every argument check happens before the first HIP call, so a rejected call
+// enqueues nothing and needs no GPU.  The library allocates no device memory.
+#include <cmath>
+#include <cstdint>
+
+#include "mla_decode.h"
+#include "mla_internal.h"
+
+using namespace mla;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_sizes(int batch, int s_q, int heads, int num_wg) {
+  if (batch < 0 || s_q < 1 || heads < 1 || num_wg < 1) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)s_q * heads > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
+  if (num_wg > 65535) return MLA_ERR_UNSUPPORTED;
+  // segment count and table sizes must stay within int32 device indexing
+  if ((int64_t)batch * num_groups(s_q, heads) > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_device_workgroups(int device, int* num_workgroups) {
+  if (!num_workgroups) return MLA_ERR_INVALID_ARG;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    return MLA_ERR_HIP;
+  *num_workgroups = cus;
+  return MLA_OK;
+}
+
+int mla_plan_size(int batch, int s_q, int num_heads, int num_workgroups, size_t* meta_bytes,
+                  size_t* workspace_bytes) {
+  if (!meta_bytes || !workspace_bytes) return MLA_ERR_INVALID_ARG;
+  int rc = check_sizes(batch, s_q, num_heads, num_workgroups);
+  if (rc) return rc;
+  *meta_bytes = meta_words(batch, s_q, num_heads, num_workgroups) * sizeof(int32_t);
+  *workspace_bytes = mla::workspace_bytes(batch, s_q, num_heads, num_workgroups);
+  return MLA_OK;
+}
+
+int mla_get_split_metadata(const int32_t* seqlens, int batch, int s_q, int num_heads, int causal,
+                           int max_blocks_per_seq, int num_workgroups, int min_split_blocks,
+                           int32_t* meta, size_t meta_bytes, void* stream) {
+  int rc = check_sizes(batch, s_q, num_heads, num_workgroups);
+  if (rc) return rc;
+  if (!meta || (batch > 0 && !seqlens)) return MLA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq < 0 || min_split_blocks < 0) return MLA_ERR_INVALID_ARG;
+  if (meta_bytes < meta_words(batch, s_q, num_heads, num_workgroups) * sizeof(int32_t))
+    return MLA_ERR_PLAN;
+  if (launch_sched(seqlens, batch, s_q, num_heads, causal, max_blocks_per_seq, num_workgroups,
+                   min_split_blocks, meta, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Stage { kStageMain = 1, kStageCombine = 2 };
+
+int decode(int stages, int dtype, const void* q, const void* kv_cache, int64_t num_blocks,
+           const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens,
+           int batch, int s_q, int num_heads, int causal, float scale, float* out, float* lse,
+           int32_t* meta, size_t meta_bytes, int num_workgroups, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  int rc = check_sizes(batch, s_q, num_heads, num_workgroups);
+  if (rc) return rc;
+  if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  if (num_blocks < 0 || max_blocks_per_seq < 0) return MLA_ERR_INVALID_ARG;
+  if (!meta) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!q || !out || !lse || !seqlens || !block_table) return MLA_ERR_INVALID_ARG;
+  if (num_blocks > 0 && !kv_cache) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (kv_cache && !aligned16(kv_cache)))
+    return MLA_ERR_INVALID_ARG;
+  if (meta_bytes < meta_words(batch, s_q, num_heads, num_workgroups) * sizeof(int32_t))
+    return MLA_ERR_PLAN;
+  const size_t ws_need = mla::workspace_bytes(batch, s_q, num_heads, num_workgroups);
+  if (workspace_bytes < ws_need) return MLA_ERR_PLAN;
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARG;
+
+  Problem p;
+  p.q = q;
+  p.kv = kv_cache;
+  p.num_blocks = num_blocks;
+  p.block_table = block_table;
+  p.max_blocks = max_blocks_per_seq;
+  p.seqlens = seqlens;
+  p.batch = batch;
+  p.s_q = s_q;
+  p.heads = num_heads;
+  p.causal = causal;
+  p.scale = scale;
+  p.out = out;
+  p.lse = lse;
+  p.meta = meta;
+  p.num_wg = num_workgroups;
+  const size_t slots = num_slots(batch, s_q, num_heads, num_workgroups);
+  p.part_o = (float*)workspace;
+  p.part_lse = p.part_o + slots * kGroupRows * kDv;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (stages & kStageMain) {
+    hipError_t e = dtype == MLA_DTYPE_BF16 ? launch_main_bf16(p, st) : launch_main_f32(p, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
+  if (stages & kStageCombine) {
+    if (launch_combine(p, st) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+#define MLA_DECODE_ARGS                                                                      \
+  int dtype, const void *q, const void *kv_cache, int64_t num_blocks,                       \
+      const int32_t *block_table, int max_blocks_per_seq, const int32_t *seqlens, int batch, \
+      int s_q, int num_heads, int causal, float scale, float *out, float *lse,               \
+      int32_t *meta, size_t meta_bytes, int num_workgroups, void *workspace,                 \
+      size_t workspace_bytes, void *stream
+#define MLA_DECODE_PASS                                                                      \
+  dtype, q, kv_cache, num_blocks, block_table, max_blocks_per_seq, seqlens, batch, s_q,     \
+      num_heads, causal, scale, out, lse, meta, meta_bytes, num_workgroups, workspace,       \
+      workspace_bytes, stream
+
+int mla_decode_fwd(MLA_DECODE_ARGS) {
+  return decode(kStageMain | kStageCombine, MLA_DECODE_PASS);
+}
+int mla_decode_main(MLA_DECODE_ARGS) { return decode(kStageMain, MLA_DECODE_PASS); }
+int mla_decode_combine(MLA_DECODE_ARGS) { return decode(kStageCombine, MLA_DECODE_PASS); }
+
+int mla_read_status(const int32_t* meta, void* stream, int32_t* status) {
+  if (!meta || !status) return MLA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, meta + H_STATUS, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MLA_ERR_HIP;
+  *status = v;
+  return MLA_OK;
+}
+
+const char* mla_status_string(int code) {
+  switch (code) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dtype or size";
+    case MLA_ERR_PLAN: return "metadata or workspace buffer too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status code";
+  }
+}
+
+}  // extern "C"

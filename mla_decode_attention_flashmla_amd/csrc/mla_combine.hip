@@ -1,0 +1,121 @@
+// Log-sum-exp combine of split parts.
+//
+// A segment (sequence, 128-row group) whose blocks were spread over several
+// workgroups left one partial (O_i normalised over its own keys, LSE_i) per
+// part.  Over the union of the parts' keys:
+//   LSE = M + ln sum_i exp(LSE_i - M),  M = max_i LSE_i
+//   O   = sum_i exp(LSE_i - LSE) * O_i
+// Parts with no visible key (LSE_i = -inf) carry weight 0.  Segments with no
+// part at all (length 0, or an invalid length) are written here too: O = 0 and
+// LSE = -inf, or NaN for invalid lengths.  Long contexts (the 128K sparse-MLA
+// case of the Triton-TLE talk's performance section) are what make splitting,
+// and so this merge, necessary when few sequences must fill all compute units.
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = 4;  // 64 threads per row, 8 columns per thread
+constexpr int kMaxSplitsLds = 1024;
+
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(
+    int batch, int s_q, int heads, int nwg, float* __restrict__ out, float* __restrict__ lse_out,
+    const int32_t* __restrict__ meta, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse) {
+  __shared__ float w_s[kRowsPerBlock][kMaxSplitsLds];
+  __shared__ float lse_s[kRowsPerBlock];
+  const int seg = blockIdx.x;
+  // a plan for other sizes was already flagged by the main kernel; touch nothing
+  if (meta[H_MAGIC] != kMagic || meta[H_BATCH] != batch || meta[H_SQ] != s_q ||
+      meta[H_HEADS] != heads || meta[H_NUM_WG] != nwg)
+    return;
+  const int groups = meta[H_NUM_GROUPS];
+  const int32_t* sr = meta + kHdrWords + (size_t)kWgWords * nwg + (size_t)seg * kSegWords;
+  const int nsplit = sr[S_NSPLIT];
+  if (nsplit == 1) return;
+  const int M = s_q * heads;
+  const int b = seg / groups, rg = seg - b * groups;
+  const int rows_in_group = min(kGroupRows, M - rg * kGroupRows);
+  const int rl = threadIdx.x >> 6;            // row within this block
+  const int lane = threadIdx.x & 63;
+  const int row_in_group = blockIdx.y * kRowsPerBlock + rl;
+  const bool row_ok = row_in_group < rows_in_group;
+  const int row = rg * kGroupRows + row_in_group;
+  const int t = row / heads, hd = row - t * heads;
+  const size_t ri = ((size_t)b * s_q + t) * heads + hd;
+
+  if (nsplit == 0) {
+    if (!row_ok) return;
+    const float fill = sr[S_SEQLEN] < 0 ? __builtin_nanf("") : 0.f;
+    float4 v = make_float4(fill, fill, fill, fill);
+    float4* o = (float4*)(out + ri * kDv) + 2 * lane;
+    o[0] = v;
+    o[1] = v;
+    if (lane == 0) lse_out[ri] = sr[S_SEQLEN] < 0 ? __builtin_nanf("") : -INFINITY;
+    return;
+  }
+
+  const size_t slot0 = (size_t)sr[S_SLOT];
+  // weights exp(LSE_i - LSE) for this row, computed by its 64 threads
+  float mx = -INFINITY;
+  if (row_ok)
+    for (int i = lane; i < nsplit; i += 64)
+      mx = fmaxf(mx, part_lse[(slot0 + i) * kGroupRows + row_in_group]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const float base = mx == -INFINITY ? 0.f : mx;
+  float sum = 0.f;
+  if (row_ok)
+    for (int i = lane; i < nsplit; i += 64) {
+      const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
+      const float w = l == -INFINITY ? 0.f : expf(l - base);
+      if (i < kMaxSplitsLds) w_s[rl][i] = w;
+      sum += w;
+    }
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  if (lane == 0) lse_s[rl] = sum > 0.f ? base + logf(sum) : -INFINITY;
+  __syncthreads();
+  if (!row_ok) return;
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < nsplit; ++i) {
+    float w;
+    if (i < kMaxSplitsLds) {
+      w = w_s[rl][i];
+    } else {
+      const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
+      w = l == -INFINITY ? 0.f : expf(l - base);
+    }
+    if (w == 0.f) continue;
+    const float4* p = (const float4*)(part_o + ((slot0 + i) * kGroupRows + row_in_group) * kDv) +
+                      2 * lane;
+    const float4 a = p[0], c = p[1];
+    acc[0] = fmaf(w, a.x, acc[0]);
+    acc[1] = fmaf(w, a.y, acc[1]);
+    acc[2] = fmaf(w, a.z, acc[2]);
+    acc[3] = fmaf(w, a.w, acc[3]);
+    acc[4] = fmaf(w, c.x, acc[4]);
+    acc[5] = fmaf(w, c.y, acc[5]);
+    acc[6] = fmaf(w, c.z, acc[6]);
+    acc[7] = fmaf(w, c.w, acc[7]);
+  }
+  float4* o = (float4*)(out + ri * kDv) + 2 * lane;
+  o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if (lane == 0) lse_out[ri] = lse_s[rl];
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Problem& p, hipStream_t stream) {
+  const int groups = num_groups(p.s_q, p.heads);
+  const int nseg = p.batch * groups;
+  if (nseg == 0) return hipSuccess;
+  dim3 grid(nseg, kGroupRows / kRowsPerBlock);
+  hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(kThreads), 0, stream, p.batch, p.s_q, p.heads,
+                     p.num_wg, p.out, p.lse, p.meta, p.part_o, p.part_lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,73 @@
+// Internal layout shared by the host library and the kernels of libmla_decode.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;        // tokens per KV block
+constexpr int kDqk = 576;        // latent 512 + rope 64
+constexpr int kDv = 512;         // V = first 512 columns
+constexpr int kGroupRows = 128;  // query rows (t, h) per row group, one workgroup's rows
+constexpr int kDefaultMinSplitBlocks = 8;
+
+// Scheduling metadata, int32 words.
+//   header      kHdrWords
+//   work table  num_workgroups x kWgWords   (one row per persistent workgroup slot)
+//   seg table   num_segments   x kSegWords  (one row per (sequence, row group))
+constexpr int kHdrWords = 32;
+constexpr int kWgWords = 8;
+constexpr int kSegWords = 8;
+constexpr int32_t kMagic = 0x4D4C4131;
+
+enum Hdr {
+  H_MAGIC = 0, H_BATCH, H_SQ, H_HEADS, H_CAUSAL, H_NUM_WG, H_STATUS, H_NUM_SEG,
+  H_NUM_GROUPS, H_TOTAL_BLOCKS, H_NUM_ITEMS, H_NUM_SLOTS, H_MAX_BLOCKS,
+};
+// work-table row: first segment, first block in it, last segment, end block in it (exclusive),
+// split index of the first segment.  seg_begin < 0: the slot has no work.
+enum Wg { W_SEG_BEGIN = 0, W_BLK_BEGIN, W_SEG_END, W_BLK_END, W_FIRST_SPLIT };
+// segment row: blocks, validated length (-1: invalid), block offset in the stream,
+// number of parts (0: no keys or invalid, 1: computed whole), first partial slot.
+enum Seg { S_NBLK = 0, S_SEQLEN, S_CUM, S_NSPLIT, S_SLOT, S_FIRST_ITEM };
+
+inline int num_groups(int s_q, int heads) { return (s_q * heads + kGroupRows - 1) / kGroupRows; }
+
+inline size_t meta_words(int batch, int s_q, int heads, int num_wg) {
+  return (size_t)kHdrWords + (size_t)kWgWords * num_wg +
+         (size_t)kSegWords * batch * num_groups(s_q, heads);
+}
+inline size_t num_slots(int batch, int s_q, int heads, int num_wg) {
+  return (size_t)num_wg + (size_t)batch * num_groups(s_q, heads);
+}
+// workspace: partial O [slots][128][512] fp32, then partial LSE [slots][128] fp32
+inline size_t workspace_bytes(int batch, int s_q, int heads, int num_wg) {
+  return num_slots(batch, s_q, heads, num_wg) * kGroupRows * (kDv + 1) * sizeof(float);
+}
+
+struct Problem {
+  const void* q;
+  const void* kv;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* seqlens;
+  int batch, s_q, heads, causal;
+  float scale;
+  float* out;
+  float* lse;
+  int32_t* meta;
+  int num_wg;
+  float* part_o;    // [slots][128][512]
+  float* part_lse;  // [slots][128]
+};
+
+hipError_t launch_sched(const int32_t* seqlens, int batch, int s_q, int heads, int causal,
+                        int max_blocks, int num_wg, int min_split_blocks, int32_t* meta,
+                        hipStream_t stream);
+hipError_t launch_main_bf16(const Problem& p, hipStream_t stream);
+hipError_t launch_main_f32(const Problem& p, hipStream_t stream);
+hipError_t launch_combine(const Problem& p, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,528 @@
+// MLA decode main kernel, bf16 inputs, gfx950 MFMA.
+//
+// One persistent workgroup (4 waves, one per SIMD) walks its range of 64-token
+// KV blocks.  Each block ("page") is copied once from HBM into LDS with 16-byte
+// direct-to-LDS loads and then serves as both K (all 576 columns) and V (the
+// first 512): the "each cache tile into shared memory" placement the TileLang
+// talk recommends for MLA (section "Future work").  The copy of page k+1 is in
+// flight while page k is computed: copy is its own pipeline stage, as the
+// talk's num_stages pipelining derives (section "What is TileLang?", pipeline
+// inference).
+//
+// Each wave owns 32 query rows (row = (token, head)).  Per page it computes
+//   S^T[token, row] = K . Q^T     on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q in VGPRs)
+// so that, in the accumulator layout, a lane holds one row and 16 tokens: the
+// row max and row sum are in-lane plus one permlane32 swap (the reduce from the
+// score accumulator to the per-row max whose layout follows from the GEMM's,
+// the middle step of the talk's layout inference).  Then
+//   O^T[col, row] = alpha * O^T + V^T . P^T   on the same MFMA
+// with V^T read from the same LDS page by ds_read_b64_tr_b16 and P^T taken
+// straight from the score registers (the token order of the V read matches the
+// accumulator layout, so P needs no shuffle).
+//
+// Registers: O^T (32 rows x 512 fp32 = 256 per lane) lives in the AGPRs
+// a0..a255 for a whole segment and only inline asm touches them (MFMA, zero,
+// rescale, read-out); the compiler works in VGPRs only (Q fragments, scores,
+// P, LDS fragments).  The score MFMAs are asm too, to keep their accumulators
+// in VGPRs.  Wait states the hardware needs around these MFMAs are written
+// into the asm: after the last score MFMA and the last PV MFMA of a page (before
+// VALU or AGPR reads of their results) and before the first PV MFMA (after VALU
+// writes of P and O).
+//
+// The running max is allowed to lag the true row max by up to 8 (log2 units):
+// O is only rescaled when a page raises some row's max by more than that, so
+// exp2 arguments stay <= 8 and the rescale (three VALU ops per O element) is rare.
+//
+// LDS page layout (74752 bytes, two pages double-buffered):
+//   main region  64 rows x 1040 bytes: columns 0..511, 1024 bytes + 16 pad per
+//                row (the pad staggers rows across banks for both the row-wise
+//                K reads and the transposed V reads)
+//   tail region  64 rows x 128 bytes: columns 512..575 as 8 16-byte chunks,
+//                chunk c of row r stored at position c ^ (r & 7)
+#include "mla_internal.h"
+#include "mla_decode.h"
+#include "mla_oacc_asm.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowStride = 1040;
+constexpr int kMainBytes = kPage * kRowStride;
+constexpr int kTailStride = 128;
+constexpr int kBufBytes = kMainBytes + kPage * kTailStride;
+constexpr int kKSteps = kDqk / 16;           // 36 MFMA k-steps over the 576 columns
+constexpr int kCTiles = kDv / 32;            // 16 column tiles of O^T
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kRescaleSlack = 8.0f;        // log2 units the running max may lag the true max
+constexpr float kNegBig = -1.0e30f;          // finite "no key yet" running max
+
+// 16 bytes per lane from global (SGPR base + VGPR offset) straight into LDS at
+// m0 + 16 * lane.  Issued through asm so the compiler does not wait for it before
+// unrelated LDS reads; completion is awaited explicitly with vmcnt(0).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  // both are wave-uniform by construction; readfirstlane keeps them in SGPRs
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                      __builtin_amdgcn_readfirstlane((uint32_t)a);
+  sbase = (const void*)(uintptr_t)au;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ float swap_halves_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- score MFMAs, accumulator in VGPRs ----
+__device__ __forceinline__ void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// ---- O^T tiles in AGPRs (tile ct = a[16ct .. 16ct+15]); ct is a compile-time constant ----
+#define MLA_FOR_TILES(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15)
+
+__device__ __forceinline__ void o_pv(int ct, const bf16x8& a, const bf16x8& b) {
+  switch (ct) {
+#define X(n)                                                                                  \
+  case n:                                                                                     \
+    asm volatile("v_mfma_f32_32x32x16_bf16 " MLA_OT##n ", %0, %1, " MLA_OT##n ::"v"(a), "v"(b) \
+                 : MLA_OT##n##_CLOBBER);                                                      \
+    break;
+    MLA_FOR_TILES(X)
+#undef X
+  }
+}
+// last PV MFMA of a page: wait states before any VALU/AGPR read of O^T
+__device__ __forceinline__ void o_pv_last(int ct, const bf16x8& a, const bf16x8& b) {
+  switch (ct) {
+#define X(n)                                                                             \
+  case n:                                                                                \
+    asm volatile("v_mfma_f32_32x32x16_bf16 " MLA_OT##n ", %0, %1, " MLA_OT##n "\n\t"     \
+                 "s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"v"(a), "v"(b) : MLA_OT##n##_CLOBBER); \
+    break;
+    MLA_FOR_TILES(X)
+#undef X
+  }
+}
+__device__ __forceinline__ void o_zero() {
+#define X(n) asm volatile(MLA_OT##n##_ZERO ::: MLA_OT##n##_CLOBBER);
+  MLA_FOR_TILES(X)
+#undef X
+}
+__device__ __forceinline__ void o_scale(float alpha) {
+  float t0, t1, t2, t3;
+#define X(n)                                                                         \
+  asm volatile(MLA_OT##n##_SCALE : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3) : "v"(alpha) \
+               : MLA_OT##n##_CLOBBER);
+  MLA_FOR_TILES(X)
+#undef X
+}
+__device__ __forceinline__ void o_read(int ct, float (&v)[16]) {
+  switch (ct) {
+#define X(n)                                                                                 \
+  case n:                                                                                    \
+    asm volatile(MLA_OT##n##_READ                                                            \
+                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]),    \
+                   "=v"(v[6]), "=v"(v[7]), "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), \
+                   "=v"(v[12]), "=v"(v[13]), "=v"(v[14]), "=v"(v[15]));                      \
+    break;
+    MLA_FOR_TILES(X)
+#undef X
+  }
+}
+
+__device__ __forceinline__ int sload(const int32_t* p) {
+  return __builtin_amdgcn_readfirstlane(*p);
+}
+
+struct PageSrc {
+  const char* base;   // block start in global memory
+  int valid_rows;     // rows [0, valid_rows) are real keys; later rows re-read the last one
+  bool load;          // false: bad block number, nothing is read
+};
+
+// Issue this wave's 18 of the 72 loads of one page into LDS buffer at lds_addr:
+// main rows wave, wave+4, ..., wave+60 and tail row groups wave, wave+4.  Running
+// pointers keep the per-row addresses from being precomputed and held in registers.
+__device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr, int wave,
+                                           int lane, uint32_t tail_lane_off) {
+  if (!src.load) return;
+  const int vmax = src.valid_rows - 1;
+  const uint32_t voff = (uint32_t)lane * 16u;
+  if (vmax == kPage - 1) {
+    const char* g = src.base + wave * (kDqk * 2);
+    uint32_t l = lds_addr + wave * kRowStride;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dma16(g, voff, l);
+      g += 4 * (kDqk * 2);
+      l += 4 * kRowStride;
+    }
+  } else {
+    int r = wave;
+    uint32_t l = lds_addr + wave * kRowStride;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rs = r < vmax ? r : vmax;
+      dma16(src.base + rs * (kDqk * 2), voff, l);
+      r += 4;
+      l += 4 * kRowStride;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int g = wave + 4 * i;  // rows 8g .. 8g+7
+    int row = 8 * g + (lane >> 3);
+    row = row < vmax ? row : vmax;
+    dma16(src.base, (uint32_t)row * (kDqk * 2) + tail_lane_off,
+          lds_addr + kMainBytes + 8 * g * kTailStride);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kv, int64_t num_blocks,
+    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seqlens,
+    int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
+    float* __restrict__ lse_out, int32_t* __restrict__ meta, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;     // which half of the wave (token/column sub-block)
+  const int l32 = lane & 31;   // row within the wave's 32 rows
+
+  // blockIdx -> slot: consecutive slots on the same XCD (blocks go round-robin over 8 XCDs)
+  const int nwg = gridDim.x;
+  int slot = blockIdx.x;
+  if ((nwg & 7) == 0) slot = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+
+  if (meta[H_MAGIC] != kMagic || meta[H_BATCH] != batch || meta[H_SQ] != s_q ||
+      meta[H_HEADS] != heads || meta[H_CAUSAL] != causal || meta[H_NUM_WG] != nwg ||
+      meta[H_MAX_BLOCKS] != max_blocks) {
+    if (threadIdx.x == 0) atomicOr(&meta[H_STATUS], MLA_STATUS_PLAN_MISMATCH);
+    return;
+  }
+  const int32_t* wrow = meta + kHdrWords + (size_t)slot * kWgWords;
+  const int32_t* segt = meta + kHdrWords + (size_t)kWgWords * nwg;
+  const int seg_first = sload(wrow + W_SEG_BEGIN);
+  if (seg_first < 0) return;
+  const int blk_first = sload(wrow + W_BLK_BEGIN);
+  const int seg_last = sload(wrow + W_SEG_END);
+  const int blk_last_end = sload(wrow + W_BLK_END);
+  const int split_first = sload(wrow + W_FIRST_SPLIT);
+  const int groups = sload(meta + H_NUM_GROUPS);
+  const int M = s_q * heads;
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  // tail loads: lane -> row 8g + lane/8, LDS position lane%8 holds chunk (lane%8) ^ (lane/8)
+  const uint32_t tail_lane_off = (uint32_t)((64 + ((lane & 7) ^ (lane >> 3))) * 16);
+  const float scale_log2 = scale * kLog2e;
+
+  // per-lane LDS byte offsets of the K (row-wise) and V (transposed) reads
+  const uint32_t k_off = (uint32_t)(l32 * kRowStride + h * 16);
+  const uint32_t v_off = (uint32_t)((4 * h + ((lane & 15) >> 2)) * kRowStride +
+                                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+
+  auto seg_nblk = [&](int s) { return sload(segt + (size_t)s * kSegWords + S_NBLK); };
+  auto page_src = [&](int s, int blk, bool& bad) -> PageSrc {
+    const int b = s / groups;
+    const int L = sload(segt + (size_t)s * kSegWords + S_SEQLEN);
+    int id = sload(block_table + (size_t)b * max_blocks + blk);
+    PageSrc ps;
+    ps.load = id >= 0 && (int64_t)id < num_blocks;
+    if (!ps.load) { bad = true; id = 0; }
+    ps.base = (const char*)kv + (size_t)id * (kPage * kDqk * 2);
+    const int rem = L - blk * kPage;
+    ps.valid_rows = rem < kPage ? rem : kPage;
+    return ps;
+  };
+
+  int seg = seg_first;
+  int blk = blk_first;
+  int buf = 0;
+  bool bad_block_next = false;  // a page of the next segment had a bad block number
+  {
+    PageSrc ps = page_src(seg, blk, bad_block_next);
+    issue_page(ps, lds0, wave, lane, tail_lane_off);
+  }
+
+  while (true) {
+    const int nb = seg_nblk(seg);
+    const int blk_end = seg == seg_last ? blk_last_end : nb;
+    const int b = seg / groups;
+    const int rg = seg - b * groups;
+    const int L = sload(segt + (size_t)seg * kSegWords + S_SEQLEN);
+    bool bad_block = bad_block_next;
+    bad_block_next = false;
+    const bool mismatch = sload(seqlens + b) != L;
+
+    // this lane's query row
+    const int row_in_group = wave * 32 + l32;
+    const int row = rg * kGroupRows + row_in_group;
+    const bool row_ok = row < M;
+    const int t = row_ok ? row / heads : 0;
+    const int hd = row_ok ? row - t * heads : 0;
+    const int n_row = causal ? L - s_q + 1 + t : L;
+    const int n_min = causal ? L - s_q + 1 : L;
+    const bool wave_active = rg * kGroupRows + wave * 32 < M;
+
+    // Q fragments: B operand of the score MFMA, k = 16*s + 8*h + j, column = row
+    bf16x8 qf[kKSteps];
+    {
+      const __bf16* qrow = q + (((size_t)b * s_q + t) * heads + hd) * kDqk + 8 * h;
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        if (row_ok) {
+          qf[s] = *(const bf16x8*)(qrow + 16 * s);
+        } else {
+          qf[s] = (bf16x8){};
+        }
+      }
+    }
+    o_zero();
+    // Q fragments (possibly zeroed by VALU) and O are read by asm MFMAs only after
+    // this fence and its wait states
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7" ::: "memory");
+    float m_run = kNegBig, l_run = 0.f;
+    bool first_page = true;
+
+    for (; blk < blk_end; ++blk) {
+      // where the next page comes from (this segment, or the next one with blocks)
+      int nseg = seg, nblk = blk + 1;
+      bool has_next = true;
+      if (nblk >= blk_end) {
+        nseg = seg + 1;
+        nblk = 0;
+        while (nseg <= seg_last && seg_nblk(nseg) == 0) ++nseg;
+        has_next = nseg <= seg_last;
+      }
+      wait_dma();
+      __syncthreads();
+      if (has_next) {
+        PageSrc ps = page_src(nseg, nblk, nseg == seg ? bad_block : bad_block_next);
+        issue_page(ps, lds0 + (buf ^ 1) * kBufBytes, wave, lane, tail_lane_off);
+      }
+      if (!wave_active) { buf ^= 1; continue; }
+
+      const lds_char* page = (const lds_char*)(uintptr_t)(lds0 + buf * kBufBytes);
+      // ---- scores S^T = K . Q^T, two 32-token tiles ----
+      // K fragments are read one k-step ahead of the MFMAs that use them; the
+      // scheduling fences keep the compiler from hoisting every read (and its
+      // registers) to the top.
+      f32x16 sacc[2];
+      auto kfrag = [&](int s, int T) -> bf16x8 {
+        const lds_char* a;
+        if (s < 32) {
+          a = page + k_off + T * 32 * kRowStride + s * 32;
+        } else {
+          const int c = (2 * (s - 32) + h) ^ (lane & 7);
+          a = page + kMainBytes + (T * 32 + l32) * kTailStride + c * 16;
+        }
+        return *(const bf16x8*)a;
+      };
+      bf16x8 kf0 = kfrag(0, 0), kf1 = kfrag(0, 1);
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        bf16x8 nk0 = kf0, nk1 = kf1;
+        if (s + 1 < kKSteps) {
+          nk0 = kfrag(s + 1, 0);
+          nk1 = kfrag(s + 1, 1);
+        }
+        if (s == 0) {
+          mfma_s_first(sacc[0], kf0, qf[s]);
+          mfma_s_first(sacc[1], kf1, qf[s]);
+        } else if (s + 1 < kKSteps) {
+          mfma_s(sacc[0], kf0, qf[s]);
+          mfma_s(sacc[1], kf1, qf[s]);
+        } else {
+          mfma_s(sacc[0], kf0, qf[s]);
+          mfma_s_last(sacc[1], kf1, qf[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        kf0 = nk0;
+        kf1 = nk1;
+      }
+      // ---- mask + online softmax (log2 domain) ----
+      const int tok0 = blk * kPage;
+      const bool need_mask = tok0 + kPage > n_min;
+      float mx = kNegBig;
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sacc[T][r] * scale_log2;
+          if (need_mask) {
+            const int tok = tok0 + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
+            v = tok < n_row ? v : -INFINITY;
+          }
+          sacc[T][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      mx = swap_halves_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
+        if (!first_page) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+          o_scale(alpha);
+        }
+        m_run = m_new;
+      }
+      first_page = false;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            e[j] = __builtin_amdgcn_exp2f(sacc[T][8 * g + j] - m_run);
+            l_run += e[j];
+          }
+          u32x4 pk = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]),
+                      pack_bf16(e[6], e[7])};
+          pf[2 * T + g] = __builtin_bit_cast(bf16x8, pk);
+        }
+      }
+      // ---- O^T += V^T . P^T ----
+      auto vfrag = [&](int kc, int ct) -> bf16x8 {
+        const lds_char* a = page + v_off + (16 * kc) * kRowStride + ct * 64;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)a);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3)))*)(a + 8 * kRowStride));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      // P and (after a rescale or zeroing) O were just written by VALU: fence the
+      // scheduler, then wait states before the first MFMA reads them
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7" ::: "memory");
+      bf16x8 vf = vfrag(0, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * kCTiles; ++i) {
+        const int kc = i / kCTiles, ct = i % kCTiles;
+        bf16x8 nv = vf;
+        if (i + 1 < 4 * kCTiles) nv = vfrag((i + 1) / kCTiles, (i + 1) % kCTiles);
+        if (i + 1 < 4 * kCTiles) {
+          o_pv(ct, vf, pf[kc]);
+        } else {
+          o_pv_last(ct, vf, pf[kc]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        vf = nv;
+      }
+      buf ^= 1;
+    }
+
+    // ---- epilogue: this segment's rows, whole or as one part ----
+    const bool bad = bad_block || mismatch;
+    if (wave_active) {
+      const int nsplit = sload(segt + (size_t)seg * kSegWords + S_NSPLIT);
+      const bool whole = nsplit == 1;
+      const float l_tot = swap_halves_sum(l_run);
+      float inv, lse_v;
+      if (bad) {
+        inv = __builtin_nanf("");
+        lse_v = __builtin_nanf("");
+      } else if (l_tot > 0.f) {
+        inv = 1.0f / l_tot;
+        lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      } else {
+        inv = 0.f;
+        lse_v = -INFINITY;
+      }
+      float* orow;
+      float* lrow;
+      if (whole) {
+        const size_t ri = ((size_t)b * s_q + t) * heads + hd;
+        orow = out + ri * kDv;
+        lrow = lse_out + ri;
+      } else {
+        const int split = seg == seg_first ? split_first : 0;
+        const size_t slot_i = (size_t)sload(segt + (size_t)seg * kSegWords + S_SLOT) + split;
+        orow = part_o + (slot_i * kGroupRows + row_in_group) * kDv;
+        lrow = part_lse + slot_i * kGroupRows + row_in_group;
+      }
+#pragma unroll
+      for (int ct = 0; ct < kCTiles; ++ct) {
+        float v[16];
+        o_read(ct, v);
+        if (row_ok) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            f32x4 o4 = {v[4 * qd] * inv, v[4 * qd + 1] * inv, v[4 * qd + 2] * inv,
+                        v[4 * qd + 3] * inv};
+            *(f32x4*)(orow + 32 * ct + 8 * qd + 4 * h) = o4;
+          }
+        }
+      }
+      if (row_ok && h == 0) *lrow = lse_v;
+    }
+    if (bad && threadIdx.x == 0)
+      atomicOr(&meta[H_STATUS], (bad_block ? MLA_STATUS_BAD_BLOCK : 0) |
+                                    (mismatch ? MLA_STATUS_PLAN_MISMATCH : 0));
+
+    // next segment with blocks
+    int nseg = seg + 1;
+    while (nseg <= seg_last && seg_nblk(nseg) == 0) ++nseg;
+    if (nseg > seg_last) break;
+    seg = nseg;
+    blk = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_main_bf16(const Problem& p, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_main_bf16_kernel, dim3(p.num_wg), dim3(kThreads), 0, stream,
+                     (const __bf16*)p.q, (const __bf16*)p.kv, p.num_blocks, p.block_table,
+                     p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal, p.scale, p.out,
+                     p.lse, p.meta, p.part_o, p.part_lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports what include/mla_decode.h declares, and rejects bad
+arguments on the host before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_decode_attention_flashmla_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "mla_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmla_decode.so not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mla_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    assert B.status_string(B.MLA_OK) == "ok"
+    for c in (B.MLA_ERR_INVALID_ARG, B.MLA_ERR_UNSUPPORTED, B.MLA_ERR_PLAN, B.MLA_ERR_HIP):
+        assert B.status_string(c) not in ("ok", "unknown status code")
+    assert B.status_string(12345) == "unknown status code"
+
+
+def test_plan_size(lib):
+    meta, ws = B.plan_size(64, 1, 128, 256)
+    assert meta == (32 + 8 * 256 + 8 * 64) * 4
+    assert ws == (256 + 64) * 128 * 513 * 4
+    meta2, ws2 = B.plan_size(128, 2, 128, 256)   # two 128-row groups per sequence
+    assert meta2 == (32 + 8 * 256 + 8 * 256) * 4
+    with pytest.raises(B.MlaError) as e:
+        B.plan_size(1, 2, 1024, 256)              # 2048 rows > MLA_MAX_ROWS
+    assert e.value.code == B.MLA_ERR_UNSUPPORTED
+    with pytest.raises(B.MlaError) as e:
+        B.plan_size(1, 0, 16, 256)
+    assert e.value.code == B.MLA_ERR_INVALID_ARG
+
+
+def _fwd(lib, **kw):
+    a = dict(dtype=B.MLA_DTYPE_BF16, q=4096, kv=8192, nblk=4, table=12288, maxb=4, lens=16384,
+             batch=1, s_q=1, heads=16, causal=0, scale=0.1, out=20480, lse=24576, meta=28672,
+             meta_bytes=1 << 20, nwg=8, ws=32768, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mla_decode_fwd(a["dtype"], a["q"], a["kv"], a["nblk"], a["table"], a["maxb"],
+                              a["lens"], a["batch"], a["s_q"], a["heads"], a["causal"],
+                              a["scale"], a["out"], a["lse"], a["meta"], a["meta_bytes"], a["nwg"],
+                              a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_decode_rejects_bad_arguments_without_touching_hip(lib):
+    # the pointers are fake: any call that got past validation would fail or fault,
+    # so a clean error code proves validation ran first
+    assert _fwd(lib, dtype=7) == B.MLA_ERR_UNSUPPORTED
+    assert _fwd(lib, q=None) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, q=4100) == B.MLA_ERR_INVALID_ARG            # not 16-byte aligned
+    assert _fwd(lib, out=None) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, scale=float("nan")) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, scale=float("inf")) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, causal=2) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, heads=0) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, s_q=2, heads=1000) == B.MLA_ERR_UNSUPPORTED
+    assert _fwd(lib, nwg=0) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, nwg=70000) == B.MLA_ERR_UNSUPPORTED
+    assert _fwd(lib, meta_bytes=16) == B.MLA_ERR_PLAN
+    assert _fwd(lib, ws_bytes=1024) == B.MLA_ERR_PLAN
+    assert _fwd(lib, ws=None) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, meta=None) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, nblk=-1) == B.MLA_ERR_INVALID_ARG
+    # an empty batch is a no-op: OK without any launch
+    assert _fwd(lib, batch=0, q=None, out=None) == B.MLA_OK
+
+
+def test_metadata_rejects_bad_arguments(lib):
+    f = lib.mla_get_split_metadata
+    assert f(None, 2, 1, 16, 0, 4, 8, 0, 4096, 1 << 20, None) == B.MLA_ERR_INVALID_ARG
+    assert f(4096, 2, 1, 16, 0, 4, 8, 0, None, 1 << 20, None) == B.MLA_ERR_INVALID_ARG
+    assert f(4096, 2, 1, 16, 0, 4, 8, 0, 8192, 8, None) == B.MLA_ERR_PLAN
+    assert f(4096, 2, 1, 16, 3, 4, 8, 0, 8192, 1 << 20, None) == B.MLA_ERR_INVALID_ARG
+    assert f(4096, 2, 1, 16, 0, -1, 8, 0, 8192, 1 << 20, None) == B.MLA_ERR_INVALID_ARG
+    assert f(4096, 2, 1, 16, 0, 4, 8, -3, 8192, 1 << 20, None) == B.MLA_ERR_INVALID_ARG
+
+
+def test_status_read_rejects_null(lib):
+    v = ctypes.c_int32(0)
+    assert lib.mla_read_status(None, None, ctypes.byref(v)) == B.MLA_ERR_INVALID_ARG
+    assert lib.mla_read_status(4096, None, None) == B.MLA_ERR_INVALID_ARG

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases are compared element by element in full; the full-size workloads in
+the launch configuration the bench times are compared on whole sampled
+sequences (every head, every key), the oracle computing those one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mla_decode_attention_flashmla_amd import binding as B
+from mla_decode_attention_flashmla_amd import inputs as I
+from oracle import mla_oracle as O
+
+from gpu_util import announce, check, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle(d, batches=None):
+    w = d["workload"]
+    return O.mla_decode(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], d["scale"],
+                        d["causal"], dtype=w.dtype, batches=batches)
+
+
+# ---------------------------------------------------------------- small, full comparison
+
+SMALL = [
+    # heads, s_q, causal, seqlens
+    (128, 1, False, [1, 63, 64, 65, 777]),
+    (128, 2, True, [2, 63, 64, 65, 700]),
+    (16, 1, False, [5, 130, 64]),
+    (32, 2, False, [129, 1, 300]),
+    (64, 2, True, [66, 3, 1000]),
+    (48, 3, True, [200, 3, 90]),          # 144 rows: two row groups, ragged second one
+]
+
+
+@pytest.mark.parametrize("heads,s_q,causal,lens", SMALL)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_cases(heads, s_q, causal, lens, dtype):
+    w = I.Workload("small", len(lens), s_q, heads, max(lens), dtype, 192, causal=causal,
+                   ragged=True, seed=100 + heads + s_q)
+    d = I.make_workload(w, seqlens=lens)
+    announce(f"small {dtype} H={heads} s_q={s_q} causal={causal} lens={lens}")
+    ref_o, ref_l = oracle(d)
+    for nwg, minb in ((None, 0), (7, 1), (40, 1)):
+        out, lse, status, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
+        assert status == 0
+        check(out, lse, ref_o, ref_l, dtype, what=f"nwg={nwg} min_split={minb}")
+
+
+def test_tiny_fp32_dense_config():
+    """The 1 x 16-head x 256-token fp32 config with a dense (identity-table) cache."""
+    d = I.make_workload(I.WORKLOADS["tiny_fp32_dense"])
+    announce("tiny_fp32_dense")
+    ref_o, ref_l = oracle(d)
+    out, lse, status, _ = run(d)
+    assert status == 0
+    check(out, lse, ref_o, ref_l, "f32", what="tiny_fp32_dense")
+
+
+def test_forced_splits_match_unsplit():
+    """Every block its own part (min_split_blocks=1, many workgroups) vs the default plan."""
+    w = I.Workload("split", 3, 1, 128, 3000, "bf16", 192, ragged=True, seed=31)
+    d = I.make_workload(w, seqlens=[3000, 1, 2049])
+    announce("forced splits")
+    ref_o, ref_l = oracle(d)
+    a = run(d, num_workgroups=256, min_split_blocks=1)
+    b = run(d, num_workgroups=1, min_split_blocks=0)
+    for out, lse, st, _ in (a, b):
+        assert st == 0
+        check(out, lse, ref_o, ref_l, "bf16", what="split plan")
+
+
+def test_stages_equal_fused_call():
+    w = I.Workload("st", 4, 1, 128, 2000, "bf16", 192, ragged=True, seed=32)
+    d = I.make_workload(w)
+    t = to_device(d)
+    announce("stage calls vs fused")
+    out_a, lse_a, _, plan = run(d, t, num_workgroups=64, min_split_blocks=1)
+    out = torch.empty((4, 1, 128, 512), device="cuda")
+    lse = torch.empty((4, 1, 128), device="cuda")
+    B.decode_main(t["q"], t["kv"], t["table"], t["lens"], float(d["scale"]), out, lse, plan)
+    B.decode_combine(t["q"], t["kv"], t["table"], t["lens"], float(d["scale"]), out, lse, plan)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), out_a) and np.array_equal(lse.cpu().numpy(), lse_a)
+
+
+def test_deterministic():
+    w = I.Workload("det", 6, 1, 128, 5000, "bf16", 192, ragged=True, seed=33)
+    d = I.make_workload(w)
+    announce("determinism")
+    a = run(d, min_split_blocks=1)
+    b = run(d, min_split_blocks=1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- definitional pins on device
+
+def test_single_key_returns_that_row_exactly():
+    w = I.Workload("one", 3, 1, 128, 1, "bf16", 192, seed=34)
+    d = I.make_workload(w)
+    announce("single key")
+    out, lse, st, _ = run(d)
+    assert st == 0
+    kv = I.bf16_bits_to_float32(d["kv_cache"])
+    for b in range(3):
+        row = kv[d["block_table"][b, 0], 0, :512]
+        assert np.array_equal(out[b, 0], np.broadcast_to(row, (128, 512)))
+    ref_o, ref_l = oracle(d)
+    assert np.abs(lse - ref_l).max() < 1e-5
+
+
+def test_uniform_scores_mean_and_log_n():
+    w = I.Workload("uni", 2, 1, 128, 1000, "bf16", 192, seed=35)
+    d = I.make_workload(w, seqlens=[1000, 77])
+    d["q"][:] = 0
+    announce("uniform scores")
+    out, lse, st, _ = run(d, min_split_blocks=1, num_workgroups=9)
+    assert st == 0
+    np.testing.assert_allclose(lse[0], np.log(1000.0), atol=2e-6)
+    np.testing.assert_allclose(lse[1], np.log(77.0), atol=2e-6)
+    ref_o, _ = oracle(d)
+    assert np.abs(out - ref_o).max() < 1e-5 * np.abs(ref_o).max() + 1e-6
+
+
+def test_causal_reduction_on_device():
+    """Token 1 of a causal pair equals a 1-query decode at L; token 0 equals one at L-1."""
+    w = I.Workload("cr", 3, 2, 128, 500, "bf16", 192, causal=True, seed=36)
+    d = I.make_workload(w, seqlens=[500, 65, 2])
+    announce("causal reduction")
+    out, lse, st, _ = run(d)
+    assert st == 0
+    d1 = dict(d, q=np.ascontiguousarray(d["q"][:, 1:2]), causal=False,
+              workload=I.Workload("cr1", 3, 1, 128, 500, "bf16", 192, seed=36))
+    o1, l1, _, _ = run(d1)
+    d0 = dict(d1, q=np.ascontiguousarray(d["q"][:, 0:1]), seqlens=d["seqlens"] - 1)
+    o0, l0, _, _ = run(d0)
+    assert np.abs(out[:, 1] - o1[:, 0]).max() <= 1e-2 * np.abs(o1).max()
+    assert np.abs(out[:, 0] - o0[:, 0]).max() <= 1e-2 * np.abs(o0).max()
+    assert np.abs(lse[:, 1] - l1[:, 0]).max() < 2e-3 and np.abs(lse[:, 0] - l0[:, 0]).max() < 2e-3
+
+
+# ---------------------------------------------------------------- edge cases and failures
+
+def test_nan_tail_and_guard_blocks_do_not_leak():
+    w = I.Workload("poison", 4, 2, 128, 300, "bf16", 192, causal=True, ragged=True, seed=37)
+    lens = [300, 65, 2, 129]
+    clean = I.make_workload(w, seqlens=lens, guard_blocks=3)
+    dirty = I.make_workload(w, seqlens=lens, guard_blocks=3, poison=True)
+    announce("NaN poison")
+    a = run(clean, min_split_blocks=1, num_workgroups=16)
+    b = run(dirty, min_split_blocks=1, num_workgroups=16)
+    assert np.isfinite(b[0]).all() and np.isfinite(b[1]).all()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_zero_length_sequences():
+    w = I.Workload("zero", 4, 1, 128, 200, "bf16", 192, ragged=True, seed=38)
+    d = I.make_workload(w, seqlens=[0, 200, 0, 64])
+    announce("zero-length sequences")
+    ref_o, ref_l = oracle(d)
+    for nwg, minb in ((None, 0), (5, 1)):
+        out, lse, st, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
+        assert st == 0
+        assert np.all(out[[0, 2]] == 0) and np.all(np.isneginf(lse[[0, 2]]))
+        check(out, lse, ref_o, ref_l, "bf16", batches=[1, 3], what="zero-length batch")
+
+
+def test_all_empty_batch():
+    w = I.Workload("empty", 2, 1, 16, 1, "bf16", 192, seed=39)
+    d = I.make_workload(w, seqlens=[0, 0])
+    announce("all-empty batch")
+    out, lse, st, _ = run(d)
+    assert st == 0 and np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_invalid_lengths_flag_status_and_nan():
+    w = I.Workload("bad", 3, 2, 128, 128, "bf16", 192, causal=True, seed=40)
+    d = I.make_workload(w, seqlens=[128, 64, 64])
+    d["seqlens"] = np.array([128, -5, 1], np.int32)     # -5 invalid; 1 < s_q invalid (causal)
+    announce("invalid lengths")
+    out, lse, st, _ = run(d)
+    assert st & B.MLA_STATUS_BAD_SEQLEN
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    assert np.isnan(out[2]).all() and np.isnan(lse[2]).all()
+    ref_o, ref_l = O.mla_decode(d["q"][:1], d["kv_cache"], d["block_table"][:1],
+                                d["seqlens"][:1], d["scale"], True)
+    check(out[:1], lse[:1], ref_o, ref_l, "bf16", what="valid sequence next to invalid ones")
+
+
+def test_bad_block_number_flags_status_and_nan():
+    w = I.Workload("blk", 3, 1, 128, 200, "bf16", 192, seed=41)
+    d = I.make_workload(w)
+    d["block_table"] = d["block_table"].copy()
+    d["block_table"][1, 2] = d["kv_cache"].shape[0] + 5
+    announce("bad block number")
+    out, lse, st, _ = run(d, min_split_blocks=1, num_workgroups=8)
+    assert st & B.MLA_STATUS_BAD_BLOCK
+    assert np.isnan(out[1]).all()
+    ref_o, ref_l = oracle(d, batches=[0, 2])
+    check(out, lse, ref_o, ref_l, "bf16", batches=[0, 2], what="good sequences")
+
+
+def test_stale_plan_is_flagged():
+    w = I.Workload("stale", 2, 1, 128, 300, "bf16", 192, seed=42)
+    d = I.make_workload(w)
+    t = to_device(d)
+    announce("stale plan")
+    _, _, st, plan = run(d, t)
+    assert st == 0
+    t["lens"] = torch.tensor([300, 200], dtype=torch.int32, device="cuda")
+    out = torch.empty((2, 1, 128, 512), device="cuda")
+    lse = torch.empty((2, 1, 128), device="cuda")
+    B.decode_fwd(t["q"], t["kv"], t["table"], t["lens"], float(d["scale"]), out, lse, plan)
+    assert B.read_status(plan) & B.MLA_STATUS_PLAN_MISMATCH
+    assert np.isnan(out[1].cpu().numpy()).all()
+
+
+def test_scheduler_partition_invariants():
+    """Every block of every segment is covered by exactly one workgroup range; part counts
+    and partial slots are consistent."""
+    w = I.Workload("sch", 37, 2, 128, 5000, "bf16", 192, causal=True, ragged=True, seed=43)
+    d = I.make_workload(w)
+    d["seqlens"][5] = 2
+    t = to_device(d)
+    for nwg, minb in ((256, 0), (256, 1), (13, 3), (1000, 1)):
+        announce(f"scheduler nwg={nwg} min_split={minb}")
+        plan = B.alloc_plan(37, 2, 128, True, t["table"].shape[1], nwg)
+        B.get_split_metadata(t["lens"], plan, minb)
+        torch.cuda.synchronize()
+        m = plan.meta.cpu().numpy()
+        nseg = m[7]
+        wg = m[32:32 + 8 * nwg].reshape(nwg, 8)
+        seg = m[32 + 8 * nwg:32 + 8 * nwg + 8 * nseg].reshape(nseg, 8)
+        assert nseg == 37 * 2 and m[6] == 0
+        lens = d["seqlens"]
+        assert np.array_equal(seg[:, 0], np.repeat((lens + 63) // 64, 2))
+        cover = [np.zeros(n, int) for n in seg[:, 0]]
+        parts = np.zeros(nseg, int)
+        for r in wg:
+            if r[0] < 0:
+                continue
+            for s in range(r[0], r[2] + 1):
+                b0 = r[1] if s == r[0] else 0
+                b1 = r[3] if s == r[2] else seg[s, 0]
+                if b1 > b0:
+                    cover[s][b0:b1] += 1
+                    parts[s] += 1
+        assert all((c == 1).all() for c in cover)
+        assert np.array_equal(parts, seg[:, 3])
+        multi = seg[:, 3] > 1
+        slots = np.concatenate([np.arange(s, s + n) for s, n in zip(seg[multi, 4], seg[multi, 3])]) \
+            if multi.any() else np.zeros(0)
+        assert len(set(slots.tolist())) == len(slots) and (slots < nwg + nseg).all()
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+FULL = [("paged_b16_l4096", 16), ("ragged_b64_l8192", 8), ("gate_b64_l8192", 6),
+        ("spec_b128_sq2_l16384", 4), ("long_b4_l131072", 2)]
+
+
+@pytest.mark.parametrize("name,nsample", FULL)
+def test_full_size_workload(name, nsample):
+    w = I.WORKLOADS[name]
+    announce(f"full-size {name}: generating")
+    d = I.make_workload(w)
+    batches = I.sample_sequences(w.batch, nsample, w.seed)
+    announce(f"full-size {name}: GPU run, sampled sequences {batches.tolist()}")
+    out, lse, st, _ = run(d)
+    assert st == 0
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ref_o, ref_l = oracle(d, batches=batches)
+    check(out, lse, ref_o, ref_l, w.dtype, batches=batches, what=name)

@@ -1,0 +1,73 @@
+"""Code-generation invariants of the bf16 main kernel, checked on its gfx950 assembly (CPU).
+
+The kernel keeps the O accumulator in AGPRs a0..a255 that only its inline asm
+touches.  That is safe only if the compiler itself never allocates an AGPR and
+never spills; the asm also relies on the wait states written into it.  These
+checks rebuild the kernel's assembly with the library's flags and verify that.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from mla_decode_attention_flashmla_amd import build as Bd
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "main.s"
+    src = os.path.join(Bd.CSRC, "mla_main_bf16.hip")
+    cmd = [Bd.hipcc(), *Bd.compile_flags(), *Bd.EXTRA.get("mla_main_bf16.hip", []),
+           "--cuda-device-only", "-S", src, "-o", str(out)]
+    subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.PIPE)
+    return out.read_text()
+
+
+def _kernel_body(asm):
+    start = asm.index("mla_main_bf16_kernel")
+    start = asm.index(":\n", start)
+    return asm[start:asm.index("s_endpgm", start)]
+
+
+def test_no_spills_and_full_agpr_file(asm):
+    assert re.search(r"ScratchSize: 0\b", asm)
+    assert re.search(r"NumAgprs: 256\b", asm)
+    assert re.search(r"Occupancy: 1\b", asm)
+    assert "scratch_" not in _kernel_body(asm)
+
+
+def test_compiler_code_never_touches_agprs(asm):
+    inside, bad = False, []
+    for ln in _kernel_body(asm).splitlines():
+        if ";;#ASMSTART" in ln:
+            inside = True
+            continue
+        if ";;#ASMEND" in ln:
+            inside = False
+            continue
+        code = ln.split(";")[0]
+        if not inside and re.search(r"\ba\d+\b|\ba\[\d", code):
+            bad.append(ln.strip())
+    assert not bad, bad[:5]
+
+
+def test_mfma_count_and_no_packed_fp32(asm):
+    body = _kernel_body(asm)
+    # 72 score + 64 PV MFMAs per page, emitted once
+    assert len(re.findall(r"v_mfma_f32_32x32x16_bf16", body)) == 136
+    assert not re.search(r"v_pk_(add|mul|fma)_f32", body)
+
+
+def test_valu_writes_are_fenced_before_pv_mfmas(asm):
+    """Between the scheduling fence before the first PV MFMA and that MFMA, only the
+    wait-state nop and LDS/SALU work may appear (no VALU writes of P)."""
+    body = _kernel_body(asm)
+    first_pv = body.index("v_mfma_f32_32x32x16_bf16 a[0:15]")
+    fence = body.rindex("sched_barrier", 0, first_pv)
+    seg = body[fence:first_pv]
+    assert "s_nop 7" in seg
+    for ln in seg.splitlines():
+        code = ln.split(";")[0].strip()
+        assert not code.startswith("v_cvt") and not code.startswith("v_mul"), ln
