@@ -70,11 +70,14 @@ constexpr float kNegBig = -1.0e30f;          // finite "no key yet" running max
 // m0 + 16 * lane.  Issued through asm so the compiler does not wait for it before
 // unrelated LDS reads; completion is awaited explicitly with vmcnt(0).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  // both are wave-uniform by construction; readfirstlane keeps them in SGPRs
-  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  // both are wave-uniform by construction; readfirstlane keeps them in SGPRs.  It
+  // returns a signed int: each half goes through uint32_t so the low word is never
+  // sign-extended into the high one.
+  lds_addr = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
   const uint64_t a = (uint64_t)(uintptr_t)sbase;
-  const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
-                      __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t au = (hi << 32) | lo;
   sbase = (const void*)(uintptr_t)au;
   uint32_t saved;
   asm volatile(

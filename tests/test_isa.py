@@ -71,3 +71,12 @@ def test_valu_writes_are_fenced_before_pv_mfmas(asm):
     for ln in seg.splitlines():
         code = ln.split(";")[0].strip()
         assert not code.startswith("v_cvt") and not code.startswith("v_mul"), ln
+
+
+def test_dma_base_address_is_not_sign_extended(asm):
+    """The 64-bit page base handed to global_load_lds is rebuilt from two readfirstlane
+    halves; the low half must be zero-extended (a sign extension turned addresses with
+    bit 31 set into 0xffffffff........)."""
+    body = _kernel_body(asm)
+    assert "global_load_lds_dwordx4" in body
+    assert "s_bfe_i64" not in body
