@@ -33,12 +33,14 @@
 // O is only rescaled when a page raises some row's max by more than that, so
 // exp2 arguments stay <= 8 and the rescale (three VALU ops per O element) is rare.
 //
-// LDS page layout (74752 bytes, two pages double-buffered):
-//   main region  64 rows x 1040 bytes: columns 0..511, 1024 bytes + 16 pad per
-//                row (the pad staggers rows across banks for both the row-wise
-//                K reads and the transposed V reads)
-//   tail region  64 rows x 128 bytes: columns 512..575 as 8 16-byte chunks,
-//                chunk c of row r stored at position c ^ (r & 7)
+// LDS page layout (77824 bytes, two pages double-buffered), for 64 banks of 4 bytes:
+//   main region  columns 0..511 of row r (1024 bytes) at 1088*r + 16*((r>>2)&3).
+//                Row starts are 64*(r&3) + 16*((r>>2)&3) modulo 256 bytes, so the
+//                16 rows of a K read (ds_read_b128, same column) hit 16 different
+//                4-bank groups, and the 4 rows x 64 bytes of a transposed V read
+//                (ds_read_b64_tr_b16) hit 4 disjoint 16-bank ranges.
+//   tail region  columns 512..575 at 69632 + 128*r: 8 16-byte chunks, chunk t of
+//                row r at position t ^ ((r>>1)&7) (16 rows of one chunk: 16 groups)
 #include "mla_internal.h"
 #include "mla_decode.h"
 #include "mla_oacc_asm.h"
@@ -55,10 +57,16 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowStride = 1040;
-constexpr int kMainBytes = kPage * kRowStride;
+constexpr int kRowPitch = 1088;               // main-region row r starts at 1088*r + 16*((r>>2)&3)
+constexpr int kMainBytes = 69632;             // 64 rows
 constexpr int kTailStride = 128;
 constexpr int kBufBytes = kMainBytes + kPage * kTailStride;
+constexpr int kKDepth = 3;                    // K fragments read this many k-steps ahead
+constexpr int kVDepth = 4;                    // V fragments read this many MFMAs ahead
+
+__host__ __device__ constexpr int main_row(int r) { return kRowPitch * r + 16 * ((r >> 2) & 3); }
+static_assert(main_row(63) + 1024 <= kMainBytes, "main region");
+static_assert(main_row(16) == 17408 && main_row(12) - main_row(4) == 8736, "row offsets");
 constexpr int kKSteps = kDqk / 16;           // 36 MFMA k-steps over the 576 columns
 constexpr int kCTiles = kDv / 32;            // 16 column tiles of O^T
 constexpr float kLog2e = 1.4426950408889634f;
@@ -185,42 +193,35 @@ struct PageSrc {
   bool load;          // false: bad block number, nothing is read
 };
 
-// Issue this wave's 18 of the 72 loads of one page into LDS buffer at lds_addr:
-// main rows wave, wave+4, ..., wave+60 and tail row groups wave, wave+4.  Running
-// pointers keep the per-row addresses from being precomputed and held in registers.
-__device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr, int wave,
-                                           int lane, uint32_t tail_lane_off) {
+// One of this wave's 18 loads of a page (72 per page in all) into the LDS buffer at
+// lds_addr: i = 0..15 copies main row 16*wave + i (1 KiB, the LDS row offset is a
+// compile-time constant), i = 16, 17 copy the tail chunks of rows 16*wave + 8*(i-16)
+// .. +7.  Rows at or past valid_rows re-read the last valid row.  Spreading the 18
+// loads over the score loop keeps the copy's LDS writes from arriving in one burst.
+__device__ __forceinline__ void issue_page_part(int i, const PageSrc& src, uint32_t lds_addr,
+                                                int wave, int lane,
+                                                const uint32_t (&tail_lane_off)[2]) {
   if (!src.load) return;
   const int vmax = src.valid_rows - 1;
-  const uint32_t voff = (uint32_t)lane * 16u;
-  if (vmax == kPage - 1) {
-    const char* g = src.base + wave * (kDqk * 2);
-    uint32_t l = lds_addr + wave * kRowStride;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dma16(g, voff, l);
-      g += 4 * (kDqk * 2);
-      l += 4 * kRowStride;
-    }
+  const int r0 = 16 * wave;
+  const uint32_t lw = lds_addr + (uint32_t)main_row(r0);
+  if (i < 16) {
+    const int rs = r0 + i < vmax ? r0 + i : vmax;
+    dma16(src.base + rs * (kDqk * 2), (uint32_t)lane * 16u, lw + main_row(i));
   } else {
-    int r = wave;
-    uint32_t l = lds_addr + wave * kRowStride;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rs = r < vmax ? r : vmax;
-      dma16(src.base + rs * (kDqk * 2), voff, l);
-      r += 4;
-      l += 4 * kRowStride;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int g = wave + 4 * i;  // rows 8g .. 8g+7
-    int row = 8 * g + (lane >> 3);
+    const int t = i - 16;
+    int row = r0 + 8 * t + (lane >> 3);
     row = row < vmax ? row : vmax;
-    dma16(src.base, (uint32_t)row * (kDqk * 2) + tail_lane_off,
-          lds_addr + kMainBytes + 8 * g * kTailStride);
+    dma16(src.base, (uint32_t)row * (kDqk * 2) + tail_lane_off[t],
+          lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
   }
+}
+constexpr int kPageParts = 18;
+
+__device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr, int wave,
+                                           int lane, const uint32_t (&tail_lane_off)[2]) {
+#pragma unroll
+  for (int i = 0; i < kPageParts; ++i) issue_page_part(i, src, lds_addr, wave, lane, tail_lane_off);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
@@ -258,13 +259,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   const int M = s_q * heads;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
-  // tail loads: lane -> row 8g + lane/8, LDS position lane%8 holds chunk (lane%8) ^ (lane/8)
-  const uint32_t tail_lane_off = (uint32_t)((64 + ((lane & 7) ^ (lane >> 3))) * 16);
+  // tail loads of rows 16*wave + 8i .. +7: lane -> row 8g + lane/8 (g = 2*wave + i), LDS
+  // position lane%8, which holds chunk (lane%8) ^ ((row>>1)&7) = (lane%8) ^ ((4i + lane/16) & 7)
+  uint32_t tail_lane_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    tail_lane_off[i] = (uint32_t)((64 + ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7))) * 16);
   const float scale_log2 = scale * kLog2e;
 
   // per-lane LDS byte offsets of the K (row-wise) and V (transposed) reads
-  const uint32_t k_off = (uint32_t)(l32 * kRowStride + h * 16);
-  const uint32_t v_off = (uint32_t)((4 * h + ((lane & 15) >> 2)) * kRowStride +
+  //   K: row l32 (+32 per token tile), 16-byte chunk 2s + h
+  //   V: row 4h + (lane%16)/4 (+16 per k-chunk, +8 for the second read), columns
+  //      32ct + 16*((lane/16)&1) + 4*(lane%4)
+  const uint32_t k_off = (uint32_t)(main_row(l32) + h * 16);
+  const uint32_t v_off = (uint32_t)(main_row(4 * h + ((lane & 15) >> 2)) +
                                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
 
   auto seg_nblk = [&](int s) { return sload(segt + (size_t)s * kSegWords + S_NBLK); };
@@ -285,10 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   int blk = blk_first;
   int buf = 0;
   bool bad_block_next = false;  // a page of the next segment had a bad block number
-  {
-    PageSrc ps = page_src(seg, blk, bad_block_next);
-    issue_page(ps, lds0, wave, lane, tail_lane_off);
-  }
+  bool first_seg = true;
 
   while (true) {
     const int nb = seg_nblk(seg);
@@ -310,7 +315,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     const int n_min = causal ? L - s_q + 1 : L;
     const bool wave_active = rg * kGroupRows + wave * 32 < M;
 
-    // Q fragments: B operand of the score MFMA, k = 16*s + 8*h + j, column = row
+    // Q fragments: B operand of the score MFMA, k = 16*s + 8*h + j, column = row.  For the
+    // first segment they are requested before the first page copy, so waiting for them
+    // does not wait for the copy (loads complete in order).
     bf16x8 qf[kKSteps];
     {
       const __bf16* qrow = q + (((size_t)b * s_q + t) * heads + hd) * kDqk + 8 * h;
@@ -322,6 +329,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
           qf[s] = (bf16x8){};
         }
       }
+    }
+    if (first_seg) {
+      PageSrc ps = page_src(seg, blk, bad_block_next);
+      bad_block = bad_block_next;
+      bad_block_next = false;
+      issue_page(ps, lds0, wave, lane, tail_lane_off);
+      first_seg = false;
     }
     o_zero();
     // Q fragments (possibly zeroed by VALU) and O are read by asm MFMAs only after
@@ -343,11 +357,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       }
       wait_dma();
       __syncthreads();
-      if (has_next) {
-        PageSrc ps = page_src(nseg, nblk, nseg == seg ? bad_block : bad_block_next);
-        issue_page(ps, lds0 + (buf ^ 1) * kBufBytes, wave, lane, tail_lane_off);
+      PageSrc nps;
+      nps.load = false;
+      if (has_next) nps = page_src(nseg, nblk, nseg == seg ? bad_block : bad_block_next);
+      const uint32_t next_lds = lds0 + (buf ^ 1) * kBufBytes;
+      if (!wave_active) {
+        issue_page(nps, next_lds, wave, lane, tail_lane_off);
+        buf ^= 1;
+        continue;
       }
-      if (!wave_active) { buf ^= 1; continue; }
 
       const lds_char* page = (const lds_char*)(uintptr_t)(lds0 + buf * kBufBytes);
       // ---- scores S^T = K . Q^T, two 32-token tiles ----
@@ -358,34 +376,40 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       auto kfrag = [&](int s, int T) -> bf16x8 {
         const lds_char* a;
         if (s < 32) {
-          a = page + k_off + T * 32 * kRowStride + s * 32;
+          a = page + k_off + (main_row(32) * T) + s * 32;
         } else {
-          const int c = (2 * (s - 32) + h) ^ (lane & 7);
+          const int c = (2 * (s - 32) + h) ^ ((l32 >> 1) & 7);
           a = page + kMainBytes + (T * 32 + l32) * kTailStride + c * 16;
         }
         return *(const bf16x8*)a;
       };
-      bf16x8 kf0 = kfrag(0, 0), kf1 = kfrag(0, 1);
+      bf16x8 kf[kKDepth + 1][2];
+#pragma unroll
+      for (int s = 0; s < kKDepth; ++s) {
+        kf[s][0] = kfrag(s, 0);
+        kf[s][1] = kfrag(s, 1);
+      }
 #pragma unroll
       for (int s = 0; s < kKSteps; ++s) {
-        bf16x8 nk0 = kf0, nk1 = kf1;
-        if (s + 1 < kKSteps) {
-          nk0 = kfrag(s + 1, 0);
-          nk1 = kfrag(s + 1, 1);
+        if ((s & 1) == 0 && s / 2 < kPageParts)
+          issue_page_part(s / 2, nps, next_lds, wave, lane, tail_lane_off);
+        if (s + kKDepth < kKSteps) {
+          kf[(s + kKDepth) % (kKDepth + 1)][0] = kfrag(s + kKDepth, 0);
+          kf[(s + kKDepth) % (kKDepth + 1)][1] = kfrag(s + kKDepth, 1);
         }
+        const bf16x8& a0 = kf[s % (kKDepth + 1)][0];
+        const bf16x8& a1 = kf[s % (kKDepth + 1)][1];
         if (s == 0) {
-          mfma_s_first(sacc[0], kf0, qf[s]);
-          mfma_s_first(sacc[1], kf1, qf[s]);
+          mfma_s_first(sacc[0], a0, qf[s]);
+          mfma_s_first(sacc[1], a1, qf[s]);
         } else if (s + 1 < kKSteps) {
-          mfma_s(sacc[0], kf0, qf[s]);
-          mfma_s(sacc[1], kf1, qf[s]);
+          mfma_s(sacc[0], a0, qf[s]);
+          mfma_s(sacc[1], a1, qf[s]);
         } else {
-          mfma_s(sacc[0], kf0, qf[s]);
-          mfma_s_last(sacc[1], kf1, qf[s]);
+          mfma_s(sacc[0], a0, qf[s]);
+          mfma_s_last(sacc[1], a1, qf[s]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        kf0 = nk0;
-        kf1 = nk1;
       }
       // ---- mask + online softmax (log2 domain) ----
       const int tok0 = blk * kPage;
@@ -432,31 +456,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         }
       }
       // ---- O^T += V^T . P^T ----
-      auto vfrag = [&](int kc, int ct) -> bf16x8 {
-        const lds_char* a = page + v_off + (16 * kc) * kRowStride + ct * 64;
+      auto vfrag = [&](int i) -> bf16x8 {
+        const int kc = i / kCTiles, ct = i % kCTiles;
+        const lds_char* a = page + v_off + kc * main_row(16) + ct * 64;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (s16x4 __attribute__((address_space(3)))*)a);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(a + 8 * kRowStride));
+            (s16x4 __attribute__((address_space(3)))*)(a + (main_row(12) - main_row(4))));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       // P and (after a rescale or zeroing) O were just written by VALU: fence the
       // scheduler, then wait states before the first MFMA reads them
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_nop 7" ::: "memory");
-      bf16x8 vf = vfrag(0, 0);
+      constexpr int kPv = 4 * kCTiles;
+      bf16x8 vf[kVDepth + 1];
 #pragma unroll
-      for (int i = 0; i < 4 * kCTiles; ++i) {
+      for (int i = 0; i < kVDepth; ++i) vf[i] = vfrag(i);
+#pragma unroll
+      for (int i = 0; i < kPv; ++i) {
         const int kc = i / kCTiles, ct = i % kCTiles;
-        bf16x8 nv = vf;
-        if (i + 1 < 4 * kCTiles) nv = vfrag((i + 1) / kCTiles, (i + 1) % kCTiles);
-        if (i + 1 < 4 * kCTiles) {
-          o_pv(ct, vf, pf[kc]);
+        if (i + kVDepth < kPv) vf[(i + kVDepth) % (kVDepth + 1)] = vfrag(i + kVDepth);
+        if (i + 1 < kPv) {
+          o_pv(ct, vf[i % (kVDepth + 1)], pf[kc]);
         } else {
-          o_pv_last(ct, vf, pf[kc]);
+          o_pv_last(ct, vf[i % (kVDepth + 1)], pf[kc]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        vf = nv;
       }
       buf ^= 1;
     }
