@@ -57,6 +57,8 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   }
 
   const size_t slot0 = (size_t)sr[S_SLOT];
+  // the parts must lie inside the workspace sized for this call (nwg + segments slots)
+  if (sr[S_SLOT] < 0 || slot0 + (size_t)nsplit > (size_t)nwg + (size_t)gridDim.x) return;
   // weights exp(LSE_i - LSE) for this row, computed by its 64 threads
   float mx = -INFINITY;
   if (row_ok)

@@ -19,15 +19,19 @@ constexpr int kDefaultMinSplitBlocks = 8;
 constexpr int kHdrWords = 32;
 constexpr int kWgWords = 8;
 constexpr int kSegWords = 8;
-constexpr int32_t kMagic = 0x4D4C4131;
+// identifies the plan layout below; changes whenever the layout does, so a plan written
+// under another layout is rejected instead of misread
+constexpr int32_t kMagic = 0x4D4C4132;
 
 enum Hdr {
   H_MAGIC = 0, H_BATCH, H_SQ, H_HEADS, H_CAUSAL, H_NUM_WG, H_STATUS, H_NUM_SEG,
   H_NUM_GROUPS, H_TOTAL_BLOCKS, H_NUM_ITEMS, H_NUM_SLOTS, H_MAX_BLOCKS,
 };
 // work-table row: first segment, first block in it, last segment, end block in it (exclusive),
-// split index of the first segment.  seg_begin < 0: the slot has no work.
-enum Wg { W_SEG_BEGIN = 0, W_BLK_BEGIN, W_SEG_END, W_BLK_END, W_FIRST_SPLIT };
+// split index of the first segment, and that segment's block count and length (so a
+// workgroup can start its first page without another dependent read).  seg_begin < 0:
+// the slot has no work.
+enum Wg { W_SEG_BEGIN = 0, W_BLK_BEGIN, W_SEG_END, W_BLK_END, W_FIRST_SPLIT, W_NBLK0, W_SEQLEN0 };
 // segment row: blocks, validated length (-1: invalid), block offset in the stream,
 // number of parts (0: no keys or invalid, 1: computed whole), first partial slot.
 enum Seg { S_NBLK = 0, S_SEQLEN, S_CUM, S_NSPLIT, S_SLOT, S_FIRST_ITEM };

@@ -183,6 +183,8 @@ __device__ __forceinline__ void o_read(int ct, float (&v)[16]) {
   }
 }
 
+__device__ __forceinline__ int M_rows(int s_q, int heads) { return s_q * heads; }
+
 __device__ __forceinline__ int sload(const int32_t* p) {
   return __builtin_amdgcn_readfirstlane(*p);
 }
@@ -241,21 +243,35 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   int slot = blockIdx.x;
   if ((nwg & 7) == 0) slot = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
 
-  if (meta[H_MAGIC] != kMagic || meta[H_BATCH] != batch || meta[H_SQ] != s_q ||
-      meta[H_HEADS] != heads || meta[H_CAUSAL] != causal || meta[H_NUM_WG] != nwg ||
-      meta[H_MAX_BLOCKS] != max_blocks) {
-    if (threadIdx.x == 0) atomicOr(&meta[H_STATUS], MLA_STATUS_PLAN_MISMATCH);
-    return;
-  }
+  // The header and this slot's row are read together (one round trip): the row lies
+  // inside the buffer the host validated for these sizes, and nothing read from it is
+  // used before the header check.
   const int32_t* wrow = meta + kHdrWords + (size_t)slot * kWgWords;
   const int32_t* segt = meta + kHdrWords + (size_t)kWgWords * nwg;
+  const int h_magic = sload(meta + H_MAGIC), h_batch = sload(meta + H_BATCH);
+  const int h_sq = sload(meta + H_SQ), h_heads = sload(meta + H_HEADS);
+  const int h_causal = sload(meta + H_CAUSAL), h_nwg = sload(meta + H_NUM_WG);
+  const int h_maxb = sload(meta + H_MAX_BLOCKS), groups = sload(meta + H_NUM_GROUPS);
   const int seg_first = sload(wrow + W_SEG_BEGIN);
-  if (seg_first < 0) return;
   const int blk_first = sload(wrow + W_BLK_BEGIN);
   const int seg_last = sload(wrow + W_SEG_END);
   const int blk_last_end = sload(wrow + W_BLK_END);
   const int split_first = sload(wrow + W_FIRST_SPLIT);
-  const int groups = sload(meta + H_NUM_GROUPS);
+  const int nblk_first = sload(wrow + W_NBLK0);
+  const int seqlen_first = sload(wrow + W_SEQLEN0);
+  if (h_magic != kMagic || h_batch != batch || h_sq != s_q || h_heads != heads ||
+      h_causal != causal || h_nwg != nwg || h_maxb != max_blocks) {
+    if (threadIdx.x == 0) atomicOr(&meta[H_STATUS], MLA_STATUS_PLAN_MISMATCH);
+    return;
+  }
+  if (seg_first < 0) return;
+  // ranges read from the plan stay inside this call's tables even if the plan is corrupt
+  const int nseg = batch * ((M_rows(s_q, heads) + kGroupRows - 1) / kGroupRows);
+  if (groups != (M_rows(s_q, heads) + kGroupRows - 1) / kGroupRows || seg_first >= nseg || seg_last < seg_first || seg_last >= nseg || blk_first < 0 ||
+      nblk_first < 0 || nblk_first > max_blocks || blk_last_end > max_blocks) {
+    if (threadIdx.x == 0) atomicOr(&meta[H_STATUS], MLA_STATUS_PLAN_MISMATCH);
+    return;
+  }
   const int M = s_q * heads;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
@@ -275,17 +291,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   const uint32_t v_off = (uint32_t)(main_row(4 * h + ((lane & 15) >> 2)) +
                                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
 
-  auto seg_nblk = [&](int s) { return sload(segt + (size_t)s * kSegWords + S_NBLK); };
-  auto page_src = [&](int s, int blk, bool& bad) -> PageSrc {
+  auto seg_nblk = [&](int s) {
+    const int v = sload(segt + (size_t)s * kSegWords + S_NBLK);
+    return v < 0 ? 0 : (v > max_blocks ? max_blocks : v);
+  };
+  // source of page blk of segment s (length L); ps.load is false for a block number
+  // outside the pool, which the caller records as a bad block
+  auto page_src = [&](int s, int L, int blk) -> PageSrc {
     const int b = s / groups;
-    const int L = sload(segt + (size_t)s * kSegWords + S_SEQLEN);
     int id = sload(block_table + (size_t)b * max_blocks + blk);
     PageSrc ps;
     ps.load = id >= 0 && (int64_t)id < num_blocks;
-    if (!ps.load) { bad = true; id = 0; }
+    if (!ps.load) id = 0;
     ps.base = (const char*)kv + (size_t)id * (kPage * kDqk * 2);
     const int rem = L - blk * kPage;
-    ps.valid_rows = rem < kPage ? rem : kPage;
+    ps.valid_rows = rem < 1 ? 1 : (rem < kPage ? rem : kPage);
     return ps;
   };
 
@@ -296,11 +316,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   bool first_seg = true;
 
   while (true) {
-    const int nb = seg_nblk(seg);
+    const int nb = first_seg ? nblk_first : seg_nblk(seg);
     const int blk_end = seg == seg_last ? blk_last_end : nb;
     const int b = seg / groups;
     const int rg = seg - b * groups;
-    const int L = sload(segt + (size_t)seg * kSegWords + S_SEQLEN);
+    const int L = first_seg ? seqlen_first : sload(segt + (size_t)seg * kSegWords + S_SEQLEN);
     bool bad_block = bad_block_next;
     bad_block_next = false;
     const bool mismatch = sload(seqlens + b) != L;
@@ -331,9 +351,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       }
     }
     if (first_seg) {
-      PageSrc ps = page_src(seg, blk, bad_block_next);
-      bad_block = bad_block_next;
-      bad_block_next = false;
+      PageSrc ps = page_src(seg, L, blk);
+      bad_block = bad_block || !ps.load;
       issue_page(ps, lds0, wave, lane, tail_lane_off);
       first_seg = false;
     }
@@ -359,7 +378,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       __syncthreads();
       PageSrc nps;
       nps.load = false;
-      if (has_next) nps = page_src(nseg, nblk, nseg == seg ? bad_block : bad_block_next);
+      if (has_next) {
+        if (nseg == seg) {
+          nps = page_src(nseg, L, nblk);
+          bad_block = bad_block || !nps.load;
+        } else {
+          nps = page_src(nseg, sload(segt + (size_t)nseg * kSegWords + S_SEQLEN), nblk);
+          bad_block_next = bad_block_next || !nps.load;
+        }
+      }
       const uint32_t next_lds = lds0 + (buf ^ 1) * kBufBytes;
       if (!wave_active) {
         issue_page(nps, next_lds, wave, lane, tail_lane_off);

@@ -49,10 +49,17 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
   const int split_first = wrow[W_FIRST_SPLIT];
   const int groups = meta[H_NUM_GROUPS];
   const int M = s_q * heads;
+  // ranges read from the plan stay inside this call's tables even if the plan is corrupt
+  const int nseg = batch * ((M + kGroupRows - 1) / kGroupRows);
+  if (groups != (M + kGroupRows - 1) / kGroupRows || seg_first >= nseg || seg_last < seg_first ||
+      seg_last >= nseg || blk_first < 0 || blk_last_end > max_blocks) {
+    if (tid == 0) atomicOr(&meta[H_STATUS], MLA_STATUS_PLAN_MISMATCH);
+    return;
+  }
 
   for (int seg = seg_first; seg <= seg_last; ++seg) {
     const int32_t* sr = segt + (size_t)seg * kSegWords;
-    const int nb = sr[S_NBLK];
+    const int nb = min(max(sr[S_NBLK], 0), max_blocks);
     if (nb == 0) continue;
     const int L = sr[S_SEQLEN];
     const int b = seg / groups;

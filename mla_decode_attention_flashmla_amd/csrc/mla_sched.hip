@@ -7,40 +7,39 @@
 // whose results are merged by log-sum-exp (the "tile configuration" the
 // DeepSeek MLA example of the TileLang talk leaves to its author: how many
 // blocks, and which work each one takes).
+//
+// Per-segment arrays live in LDS when they fit (up to kLdsSegs segments);
+// larger batches keep them in the metadata buffer itself.  Prefix sums are
+// thread-local runs plus one wave-shuffle scan of the 256 run totals.
 #include "mla_internal.h"
+#include "mla_decode.h"
 
 namespace mla {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kLdsSegs = 4096;
 
-// Exclusive prefix sum of seg[i*kSegWords + src] into seg[i*kSegWords + dst] for i < n,
-// by the whole block, in chunks of kThreads.  Returns the total (in every thread).
-__device__ int64_t block_exclusive_scan(int32_t* seg, int n, int src, int dst, bool only_multi,
-                                        int64_t* lds) {
-  int64_t carry = 0;
-  const int tid = threadIdx.x;
-  for (int base = 0; base < n; base += kThreads) {
-    int i = base + tid;
-    int64_t v = 0;
-    if (i < n) {
-      v = seg[(size_t)i * kSegWords + src];
-      if (only_multi && v < 2) v = 0;
-    }
-    lds[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      int64_t add = tid >= off ? lds[tid - off] : 0;
-      __syncthreads();
-      lds[tid] += add;
-      __syncthreads();
-    }
-    if (i < n) seg[(size_t)i * kSegWords + dst] = (int32_t)(carry + lds[tid] - v);
-    int64_t chunk_total = lds[kThreads - 1];
-    __syncthreads();
-    carry += chunk_total;
+// Exclusive prefix sum over the block of one value per thread; returns the total.
+__device__ int64_t block_scan_exclusive(int64_t v, int64_t& total, int64_t* wave_tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int64_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
   }
-  return carry;
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    if (w < wave) before += wave_tot[w];
+    all += wave_tot[w];
+  }
+  __syncthreads();
+  total = all;
+  return before + x - v;
 }
 
 // Work item holding stream position pos when T blocks are cut into n items
@@ -49,13 +48,14 @@ __device__ inline int item_of(int64_t pos, int64_t T, int64_t n) {
   return (int)(((pos + 1) * n + T - 1) / T - 1);
 }
 
-// Last segment whose first block is <= pos (segments with no blocks are skipped over,
-// because the next one starts at the same position).
-__device__ inline int seg_of(const int32_t* seg, int nseg, int64_t pos) {
-  int lo = 0, hi = nseg;  // first index with cum > pos
+template <class Arr>
+__device__ inline int seg_of(const Arr& cum, int nseg, int64_t pos) {
+  // last segment whose first block is <= pos (segments with no blocks share the next
+  // one's offset, so the last such index always has blocks)
+  int lo = 0, hi = nseg;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
-    if ((int64_t)seg[(size_t)mid * kSegWords + S_CUM] > pos) hi = mid; else lo = mid + 1;
+    if ((int64_t)cum(mid) > pos) hi = mid; else lo = mid + 1;
   }
   return lo - 1;
 }
@@ -63,37 +63,49 @@ __device__ inline int seg_of(const int32_t* seg, int nseg, int64_t pos) {
 __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
     const int32_t* __restrict__ seqlens, int batch, int s_q, int heads, int causal,
     int max_blocks, int num_wg, int min_split_blocks, int32_t* __restrict__ meta) {
-  __shared__ int64_t lds[kThreads];
+  __shared__ int32_t l_nblk[kLdsSegs], l_cum[kLdsSegs];
+  __shared__ int64_t wave_tot[kThreads / 64];
   __shared__ int status_lds;
   const int tid = threadIdx.x;
   const int groups = (s_q * heads + kGroupRows - 1) / kGroupRows;
   const int nseg = batch * groups;
+  const bool in_lds = nseg <= kLdsSegs;
   int32_t* wg = meta + kHdrWords;
   int32_t* seg = wg + (size_t)kWgWords * num_wg;
+  auto NB = [&](int s) -> int32_t& { return in_lds ? l_nblk[s] : seg[(size_t)s * kSegWords + S_NBLK]; };
+  auto CUM = [&](int s) -> int32_t& { return in_lds ? l_cum[s] : seg[(size_t)s * kSegWords + S_CUM]; };
 
   if (tid == 0) status_lds = 0;
   __syncthreads();
 
-  // 1. per segment: validated length and block count
+  // 1. validated length and block count of every segment
   const int64_t cap = (int64_t)max_blocks * kPage;
   for (int s = tid; s < nseg; s += kThreads) {
-    int b = s / groups;
-    int L = seqlens[b];
-    bool ok = L >= 0 && (int64_t)L <= cap && (!causal || L >= s_q);
+    const int b = s / groups;
+    const int L = seqlens[b];
+    const bool ok = L >= 0 && (int64_t)L <= cap && (!causal || L >= s_q);
+    const int nb = ok ? (L + kPage - 1) / kPage : 0;
+    NB(s) = nb;
     int32_t* r = seg + (size_t)s * kSegWords;
-    r[S_NBLK] = ok ? (L + kPage - 1) / kPage : 0;
+    r[S_NBLK] = nb;
     r[S_SEQLEN] = ok ? L : -1;
-    if (!ok) atomicOr(&status_lds, 1);
-  }
-  for (int w = tid; w < num_wg; w += kThreads) {
-    int32_t* r = wg + (size_t)w * kWgWords;
-    r[W_SEG_BEGIN] = -1;
-    r[W_BLK_BEGIN] = r[W_SEG_END] = r[W_BLK_END] = r[W_FIRST_SPLIT] = 0;
+    if (!ok) atomicOr(&status_lds, MLA_STATUS_BAD_SEQLEN);
   }
   __syncthreads();
 
-  // 2. block offset of every segment in the stream
-  const int64_t T = block_exclusive_scan(seg, nseg, S_NBLK, S_CUM, false, lds);
+  // 2. block offset of every segment in the stream (thread-local runs + block scan)
+  const int per = (nseg + kThreads - 1) / kThreads;
+  const int r0 = min(nseg, tid * per), r1 = min(nseg, r0 + per);
+  int64_t run = 0;
+  for (int s = r0; s < r1; ++s) run += NB(s);
+  int64_t T;
+  int64_t acc = block_scan_exclusive(run, T, wave_tot);
+  for (int s = r0; s < r1; ++s) {
+    const int nb = NB(s);
+    CUM(s) = (int32_t)acc;
+    seg[(size_t)s * kSegWords + S_CUM] = (int32_t)acc;
+    acc += nb;
+  }
   __syncthreads();
 
   // 3. cut the stream into n items, spread over the slots
@@ -102,36 +114,61 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
   if (n < 1) n = 1;
   if (n > num_wg) n = num_wg;
   if (T == 0) n = 0;
-  for (int64_t k = tid; k < n; k += kThreads) {
-    int64_t begin = k * T / n, end = (k + 1) * T / n;
-    int sb = seg_of(seg, nseg, begin), se = seg_of(seg, nseg, end - 1);
-    int slot = (int)(k * num_wg / n);
-    int32_t* r = wg + (size_t)slot * kWgWords;
-    int64_t cb = seg[(size_t)sb * kSegWords + S_CUM];
+  auto cum_at = [&](int s) { return CUM(s); };
+  for (int w = tid; w < num_wg; w += kThreads) {
+    int32_t* r = wg + (size_t)w * kWgWords;
+    // slot w holds item k iff k*num_wg/n == w for some k
+    int k = -1;
+    if (n > 0) {
+      const int64_t kk = ((int64_t)w * n + num_wg - 1) / num_wg;  // smallest k with k*W/n >= w
+      if (kk < n && kk * num_wg / n == w) k = (int)kk;
+    }
+    if (k < 0) {
+      r[W_SEG_BEGIN] = -1;
+      r[W_BLK_BEGIN] = r[W_SEG_END] = r[W_BLK_END] = r[W_FIRST_SPLIT] = 0;
+      r[W_NBLK0] = r[W_SEQLEN0] = 0;
+      continue;
+    }
+    const int64_t begin = (int64_t)k * T / n, end = (int64_t)(k + 1) * T / n;
+    const int sb = seg_of(cum_at, nseg, begin), se = seg_of(cum_at, nseg, end - 1);
+    const int64_t cb = CUM(sb);
     r[W_SEG_BEGIN] = sb;
     r[W_BLK_BEGIN] = (int32_t)(begin - cb);
     r[W_SEG_END] = se;
-    r[W_BLK_END] = (int32_t)(end - seg[(size_t)se * kSegWords + S_CUM]);
+    r[W_BLK_END] = (int32_t)(end - CUM(se));
     r[W_FIRST_SPLIT] = (int32_t)(k - item_of(cb, T, n));
+    r[W_NBLK0] = NB(sb);
+    r[W_SEQLEN0] = seg[(size_t)sb * kSegWords + S_SEQLEN];
   }
-  // 4. parts per segment
-  for (int s = tid; s < nseg; s += kThreads) {
-    int32_t* r = seg + (size_t)s * kSegWords;
-    int nb = r[S_NBLK];
-    if (nb == 0) {
-      r[S_NSPLIT] = 0;
-      r[S_FIRST_ITEM] = -1;
-    } else {
-      int64_t c = r[S_CUM];
-      int first = item_of(c, T, n), last = item_of(c + nb - 1, T, n);
-      r[S_NSPLIT] = last - first + 1;
-      r[S_FIRST_ITEM] = first;
+
+  // 4. parts per segment, 5. partial slots of segments computed in several parts
+  run = 0;
+  for (int s = r0; s < r1; ++s) {
+    const int nb = NB(s);
+    int ns = 0;
+    if (nb) {
+      const int64_t c = CUM(s);
+      ns = item_of(c + nb - 1, T, n) - item_of(c, T, n) + 1;
     }
+    if (ns > 1) run += ns;
+  }
+  int64_t slots;
+  acc = block_scan_exclusive(run, slots, wave_tot);
+  for (int s = r0; s < r1; ++s) {
+    int32_t* r = seg + (size_t)s * kSegWords;
+    const int nb = NB(s);
+    int ns = 0, first = -1;
+    if (nb) {
+      const int64_t c = CUM(s);
+      first = item_of(c, T, n);
+      ns = item_of(c + nb - 1, T, n) - first + 1;
+    }
+    r[S_NSPLIT] = ns;
+    r[S_FIRST_ITEM] = first;
+    r[S_SLOT] = (int32_t)acc;
+    if (ns > 1) acc += ns;
   }
   __syncthreads();
-
-  // 5. partial slots of segments computed in several parts
-  const int64_t slots = block_exclusive_scan(seg, nseg, S_NSPLIT, S_SLOT, true, lds);
 
   if (tid == 0) {
     meta[H_MAGIC] = kMagic;
