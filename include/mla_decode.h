@@ -58,7 +58,7 @@ extern "C" {
 
 /* Return codes. */
 #define MLA_OK 0
-#define MLA_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, misalignment, non-finite scale */
+#define MLA_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, misalignment, scale not finite and > 0 */
 #define MLA_ERR_UNSUPPORTED (-2) /* unknown dtype, s_q * num_heads above MLA_MAX_ROWS */
 #define MLA_ERR_PLAN (-3)        /* metadata or workspace buffer too small for these sizes */
 #define MLA_ERR_HIP (-4)         /* a HIP runtime call failed (launch, copy, device query) */
@@ -112,6 +112,7 @@ int mla_get_split_metadata(const int32_t* seqlens, int batch, int s_q, int num_h
  * workspace: device scratch of >= workspace_bytes (mla_plan_size) for the
  * partial results of split sequences; no zeroing needed.
  * dtype: MLA_DTYPE_BF16 (MFMA path) or MLA_DTYPE_F32 (fp32 path).
+ * scale: the softmax scale, finite and > 0 (e.g. 1/sqrt(192)).
  */
 int mla_decode_fwd(int dtype, const void* q, const void* kv_cache, int64_t num_blocks,
                    const int32_t* block_table, int max_blocks_per_seq,

@@ -77,7 +77,7 @@ int decode(int stages, int dtype, const void* q, const void* kv_cache, int64_t n
   int rc = check_sizes(batch, s_q, num_heads, num_workgroups);
   if (rc) return rc;
   if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if (num_blocks < 0 || max_blocks_per_seq < 0) return MLA_ERR_INVALID_ARG;
   if (!meta) return MLA_ERR_INVALID_ARG;
   if (batch == 0) return MLA_OK;

@@ -438,21 +438,27 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // ---- mask + online softmax (log2 domain) ----
+      // ---- causal / length mask, only for pages that reach past the shortest row's end ----
       const int tok0 = blk * kPage;
-      const bool need_mask = tok0 + kPage > n_min;
+      if (tok0 + kPage > n_min) {
+        asm volatile("");  // keeps this a branch rather than selects on every page
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tok = tok0 + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (tok >= n_row) sacc[T][r] = -INFINITY;
+          }
+        }
+      }
+      // ---- online softmax (log2 domain) ----
       float mx = kNegBig;
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = sacc[T][r] * scale_log2;
-          if (need_mask) {
-            const int tok = tok0 + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-            v = tok < n_row ? v : -INFINITY;
-          }
-          sacc[T][r] = v;
-          mx = fmaxf(mx, v);
+          sacc[T][r] *= scale_log2;
+          mx = fmaxf(mx, sacc[T][r]);
         }
       }
       mx = swap_halves_max(mx);

@@ -77,6 +77,9 @@ def test_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _fwd(lib, out=None) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, scale=float("nan")) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, scale=float("inf")) == B.MLA_ERR_INVALID_ARG
+    # the softmax scale is positive: the kernels take the row max on unscaled scores
+    assert _fwd(lib, scale=0.0) == B.MLA_ERR_INVALID_ARG
+    assert _fwd(lib, scale=-0.1) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, causal=2) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, heads=0) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, s_q=2, heads=1000) == B.MLA_ERR_UNSUPPORTED
