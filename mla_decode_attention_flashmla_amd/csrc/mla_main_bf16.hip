@@ -41,6 +41,8 @@
 //                (ds_read_b64_tr_b16) hit 4 disjoint 16-bank ranges.
 //   tail region  columns 512..575 at 69632 + 128*r: 8 16-byte chunks, chunk t of
 //                row r at position t ^ ((r>>1)&7) (16 rows of one chunk: 16 groups)
+#include <type_traits>
+
 #include "mla_internal.h"
 #include "mla_decode.h"
 #include "mla_oacc_asm.h"
@@ -73,6 +75,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleSlack = 8.0f;        // log2 units the running max may lag the true max
 constexpr float kNegBig = -1.0e30f;          // finite "no key yet" running max
+
+// f(integral_constant<int, I>) for I = B .. E-1: every index is a compile-time constant,
+// so the O^T tile an asm MFMA names is always resolved at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // 16 bytes per lane from global (SGPR base + VGPR offset) straight into LDS at
 // m0 + 16 * lane.  Issued through asm so the compiler does not wait for it before
@@ -506,17 +518,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       bf16x8 vf[kVDepth + 1];
 #pragma unroll
       for (int i = 0; i < kVDepth; ++i) vf[i] = vfrag(i);
-#pragma unroll
-      for (int i = 0; i < kPv; ++i) {
-        const int kc = i / kCTiles, ct = i % kCTiles;
-        if (i + kVDepth < kPv) vf[(i + kVDepth) % (kVDepth + 1)] = vfrag(i + kVDepth);
-        if (i + 1 < kPv) {
+      auto pv_step = [&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        constexpr int kc = i / kCTiles, ct = i % kCTiles;
+        if constexpr (i + kVDepth < kPv) vf[(i + kVDepth) % (kVDepth + 1)] = vfrag(i + kVDepth);
+        if constexpr (i + 1 < kPv) {
           o_pv(ct, vf[i % (kVDepth + 1)], pf[kc]);
         } else {
           o_pv_last(ct, vf[i % (kVDepth + 1)], pf[kc]);
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
+      };
+      static_for<0, kPv>(pv_step);
       buf ^= 1;
     }
 
