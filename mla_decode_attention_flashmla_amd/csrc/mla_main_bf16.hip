@@ -309,9 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   };
   // source of page blk of segment s (length L); ps.load is false for a block number
   // outside the pool, which the caller records as a bad block
-  auto page_src = [&](int s, int L, int blk) -> PageSrc {
-    const int b = s / groups;
-    int id = sload(block_table + (size_t)b * max_blocks + blk);
+  auto page_src_id = [&](int L, int blk, int id) -> PageSrc {
     PageSrc ps;
     ps.load = id >= 0 && (int64_t)id < num_blocks;
     if (!ps.load) id = 0;
@@ -320,6 +318,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     ps.valid_rows = rem < 1 ? 1 : (rem < kPage ? rem : kPage);
     return ps;
   };
+  auto page_src = [&](int s, int L, int blk) -> PageSrc {
+    return page_src_id(L, blk, sload(block_table + (size_t)(s / groups) * max_blocks + blk));
+  };
+  // block number of page pre_blk of the current segment, read one page early (during
+  // the softmax, where no LDS read waits behind the scalar load)
+  int pre_id = 0, pre_blk = -1;
 
   int seg = seg_first;
   int blk = blk_first;
@@ -374,6 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7" ::: "memory");
     float m_run = kNegBig, l_run = 0.f;
+    pre_blk = -1;
     bool first_page = true;
 
     for (; blk < blk_end; ++blk) {
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       nps.load = false;
       if (has_next) {
         if (nseg == seg) {
-          nps = page_src(nseg, L, nblk);
+          nps = nblk == pre_blk ? page_src_id(L, nblk, pre_id) : page_src(nseg, L, nblk);
           bad_block = bad_block || !nps.load;
         } else {
           nps = page_src(nseg, sload(segt + (size_t)nseg * kSegWords + S_SEQLEN), nblk);
@@ -449,6 +454,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
           mfma_s_last(sacc[1], a1, qf[s]);
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (blk + 2 < blk_end) {
+        pre_blk = blk + 2;
+        pre_id = sload(block_table + (size_t)b * max_blocks + pre_blk);
       }
       // ---- causal / length mask, only for pages that reach past the shortest row's end ----
       const int tok0 = blk * kPage;

@@ -42,10 +42,19 @@ __device__ int64_t block_scan_exclusive(int64_t v, int64_t& total, int64_t* wave
   return before + x - v;
 }
 
+// floor(a / b) for 0 <= a < 2^53, b > 0, through one correctly rounded fp64 division:
+// the quotient's rounding error, at most a * 2^-53 / b, is below the 1 / b gap between
+// a non-integer quotient and the next integer, so the floor is exact (and a 64-bit
+// integer division is a long serial instruction sequence on this GPU).
+__device__ inline int64_t floordiv(int64_t a, int64_t b) {
+  return (int64_t)__builtin_floor((double)a / (double)b);
+}
+
 // Work item holding stream position pos when T blocks are cut into n items
-// (item k covers [k*T/n, (k+1)*T/n)).
+// (item k covers [k*T/n, (k+1)*T/n)).  pos < T < 2^31, n <= 65535: every operand of the
+// divisions stays below 2^47.
 __device__ inline int item_of(int64_t pos, int64_t T, int64_t n) {
-  return (int)(((pos + 1) * n + T - 1) / T - 1);
+  return (int)(floordiv((pos + 1) * n + T - 1, T) - 1);
 }
 
 template <class Arr>
@@ -110,18 +119,20 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
 
   // 3. cut the stream into n items, spread over the slots
   const int64_t minb = min_split_blocks > 0 ? min_split_blocks : kDefaultMinSplitBlocks;
-  int64_t n = T / minb;
+  int64_t n = floordiv(T, minb);
   if (n < 1) n = 1;
   if (n > num_wg) n = num_wg;
-  if (T == 0) n = 0;
+  // the plan stores block offsets in 32 bits: a longer stream gets no work and a status bit
+  if (T == 0 || T > 0x7fffffffLL) n = 0;
+  if (T > 0x7fffffffLL && tid == 0) atomicOr(&status_lds, MLA_STATUS_BAD_SEQLEN);
   auto cum_at = [&](int s) { return CUM(s); };
   for (int w = tid; w < num_wg; w += kThreads) {
     int32_t* r = wg + (size_t)w * kWgWords;
     // slot w holds item k iff k*num_wg/n == w for some k
     int k = -1;
     if (n > 0) {
-      const int64_t kk = ((int64_t)w * n + num_wg - 1) / num_wg;  // smallest k with k*W/n >= w
-      if (kk < n && kk * num_wg / n == w) k = (int)kk;
+      const int64_t kk = floordiv((int64_t)w * n + num_wg - 1, num_wg);  // smallest k with k*W/n >= w
+      if (kk < n && floordiv(kk * num_wg, n) == w) k = (int)kk;
     }
     if (k < 0) {
       r[W_SEG_BEGIN] = -1;
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
       r[W_NBLK0] = r[W_SEQLEN0] = 0;
       continue;
     }
-    const int64_t begin = (int64_t)k * T / n, end = (int64_t)(k + 1) * T / n;
+    const int64_t begin = floordiv((int64_t)k * T, n), end = floordiv((int64_t)(k + 1) * T, n);
     const int sb = seg_of(cum_at, nseg, begin), se = seg_of(cum_at, nseg, end - 1);
     const int64_t cb = CUM(sb);
     r[W_SEG_BEGIN] = sb;
