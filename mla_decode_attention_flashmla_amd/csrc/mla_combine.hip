@@ -18,6 +18,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 4;  // 64 threads per row, 8 columns per thread
 constexpr int kMaxSplitsLds = 1024;
+constexpr int kBatch = 4;         // parts whose O loads are in flight together
 
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     int batch, int s_q, int heads, int nwg, float* __restrict__ out, float* __restrict__ lse_out,
@@ -59,12 +60,34 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   const size_t slot0 = (size_t)sr[S_SLOT];
   // the parts must lie inside the workspace sized for this call (nwg + segments slots)
   if (sr[S_SLOT] < 0 || slot0 + (size_t)nsplit > (size_t)nwg + (size_t)gridDim.x) return;
+  const float* prow = part_o + (slot0 * kGroupRows + row_in_group) * kDv + 8 * lane;
+  const size_t pstride = (size_t)kGroupRows * kDv;  // floats from one part's row to the next's
+
+  // The first kBatch parts' O values are requested before the weights are known, so
+  // their latency overlaps the LSE reads (every load below is independent).
+  float4 pa[kBatch], pc[kBatch];
+  if (row_ok) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j < nsplit) {
+        pa[j] = *(const float4*)(prow + j * pstride);
+        pc[j] = *(const float4*)(prow + j * pstride + 4);
+      }
+    }
+  }
+
   // weights exp(LSE_i - LSE) for this row, computed by its 64 threads
   float mx = -INFINITY;
+  bool nan = false;
   if (row_ok)
-    for (int i = lane; i < nsplit; i += 64)
-      mx = fmaxf(mx, part_lse[(slot0 + i) * kGroupRows + row_in_group]);
+    for (int i = lane; i < nsplit; i += 64) {
+      const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
+      nan = nan || __builtin_isnan(l);
+      mx = fmaxf(mx, l);
+    }
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  // one row is one wave: any lane that read a NaN part flags the row
+  nan = __builtin_amdgcn_ballot_w64(nan) != 0;
   const float base = mx == -INFINITY ? 0.f : mx;
   float sum = 0.f;
   if (row_ok)
@@ -75,24 +98,20 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
       sum += w;
     }
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  const float inv = sum > 0.f ? 1.f / sum : 0.f;
-  if (lane == 0) lse_s[rl] = sum > 0.f ? base + logf(sum) : -INFINITY;
+  // a part flagged bad (NaN) makes the whole row NaN, O and LSE alike
+  const float inv = nan ? __builtin_nanf("") : (sum > 0.f ? 1.f / sum : 0.f);
+  if (lane == 0)
+    lse_s[rl] = nan ? __builtin_nanf("") : (sum > 0.f ? base + logf(sum) : -INFINITY);
   __syncthreads();
   if (!row_ok) return;
 
+  auto weight = [&](int i) {
+    if (i < kMaxSplitsLds) return w_s[rl][i];
+    const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
+    return l == -INFINITY ? 0.f : expf(l - base);
+  };
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < nsplit; ++i) {
-    float w;
-    if (i < kMaxSplitsLds) {
-      w = w_s[rl][i];
-    } else {
-      const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
-      w = l == -INFINITY ? 0.f : expf(l - base);
-    }
-    if (w == 0.f) continue;
-    const float4* p = (const float4*)(part_o + ((slot0 + i) * kGroupRows + row_in_group) * kDv) +
-                      2 * lane;
-    const float4 a = p[0], c = p[1];
+  auto add = [&](float w, const float4& a, const float4& c) {
     acc[0] = fmaf(w, a.x, acc[0]);
     acc[1] = fmaf(w, a.y, acc[1]);
     acc[2] = fmaf(w, a.z, acc[2]);
@@ -101,6 +120,22 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     acc[5] = fmaf(w, c.y, acc[5]);
     acc[6] = fmaf(w, c.z, acc[6]);
     acc[7] = fmaf(w, c.w, acc[7]);
+  };
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (j < nsplit) add(weight(j), pa[j], pc[j]);
+  // further parts, kBatch at a time with all their loads issued first
+  for (int i0 = kBatch; i0 < nsplit; i0 += kBatch) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (i0 + j < nsplit) {
+        pa[j] = *(const float4*)(prow + (i0 + j) * pstride);
+        pc[j] = *(const float4*)(prow + (i0 + j) * pstride + 4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (i0 + j < nsplit) add(weight(i0 + j), pa[j], pc[j]);
   }
   float4* o = (float4*)(out + ri * kDv) + 2 * lane;
   o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
