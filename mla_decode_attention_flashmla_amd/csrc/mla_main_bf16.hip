@@ -478,16 +478,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         }
       }
       // ---- online softmax (log2 domain) ----
-      float mx = kNegBig;
+      // the max is taken on raw scores (the scale is positive) and the scale is folded
+      // into the exponent's FMA
+      float mx = -INFINITY;
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[T][r] *= scale_log2;
-          mx = fmaxf(mx, sacc[T][r]);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[T][r]);
       }
-      mx = swap_halves_max(mx);
+      mx = swap_halves_max(mx) * scale_log2;
       const float m_new = fmaxf(m_run, mx);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
         if (!first_page) {
@@ -506,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
           float e[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            e[j] = __builtin_amdgcn_exp2f(sacc[T][8 * g + j] - m_run);
+            e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[T][8 * g + j], scale_log2, -m_run));
             l_run += e[j];
           }
           u32x4 pk = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]),
