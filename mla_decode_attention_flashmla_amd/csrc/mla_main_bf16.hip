@@ -204,7 +204,7 @@ __device__ __forceinline__ int sload(const int32_t* p) {
 struct PageSrc {
   const char* base;   // block start in global memory
   int valid_rows;     // rows [0, valid_rows) are real keys; later rows re-read the last one
-  bool load;          // false: bad block number, nothing is read
+  int load;           // 0: bad block number, nothing is read
 };
 
 // One of this wave's 18 loads of a page (72 per page in all) into the LDS buffer at
@@ -307,19 +307,26 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     const int v = sload(segt + (size_t)s * kSegWords + S_NBLK);
     return v < 0 ? 0 : (v > max_blocks ? max_blocks : v);
   };
-  // source of page blk of segment s (length L); ps.load is false for a block number
-  // outside the pool, which the caller records as a bad block
-  auto page_src_id = [&](int L, int blk, int id) -> PageSrc {
+  // Source of a page with `rows` valid rows (1..64) in block `id`; ps.load is 0 for a
+  // block number outside the pool, which the caller records as a bad block.  All of it
+  // is wave-uniform scalar work (one unsigned compare against the pool size clamped to
+  // 31 bits), done once per page.
+  const uint32_t pool_blocks = num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)num_blocks;
+  auto page_src_id = [&](int rows, int id) -> PageSrc {
     PageSrc ps;
-    ps.load = id >= 0 && (int64_t)id < num_blocks;
-    if (!ps.load) id = 0;
-    ps.base = (const char*)kv + (size_t)id * (kPage * kDqk * 2);
-    const int rem = L - blk * kPage;
-    ps.valid_rows = rem < 1 ? 1 : (rem < kPage ? rem : kPage);
+    ps.load = (uint32_t)id < pool_blocks ? 1 : 0;
+    ps.base = (const char*)kv + (size_t)(ps.load ? (uint32_t)id : 0u) * (kPage * kDqk * 2);
+    ps.valid_rows = rows;
     return ps;
   };
+  // valid rows of page blk of a sequence of length L, clamped to 1..64 whatever the plan says
+  auto page_rows = [](int L, int blk) {
+    const int rem = L - blk * kPage;
+    return rem < 1 ? 1 : (rem < kPage ? rem : kPage);
+  };
   auto page_src = [&](int s, int L, int blk) -> PageSrc {
-    return page_src_id(L, blk, sload(block_table + (size_t)(s / groups) * max_blocks + blk));
+    return page_src_id(page_rows(L, blk),
+                       sload(block_table + (size_t)(s / groups) * max_blocks + blk));
   };
   // block number of page pre_blk of the current segment, read one page early (during
   // the softmax, where no LDS read waits behind the scalar load)
@@ -337,6 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     const int b = seg / groups;
     const int rg = seg - b * groups;
     const int L = first_seg ? seqlen_first : sload(segt + (size_t)seg * kSegWords + S_SEQLEN);
+    const int last_rows = page_rows(L, nb - 1);
     bool bad_block = bad_block_next;
     bad_block_next = false;
     const bool mismatch = sload(seqlens + b) != L;
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     }
     if (first_seg) {
       PageSrc ps = page_src(seg, L, blk);
-      bad_block = bad_block || !ps.load;
+      bad_block = bad_block || ps.load == 0;
       issue_page(ps, lds0, wave, lane, tail_lane_off);
       first_seg = false;
     }
@@ -394,14 +402,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       wait_dma();
       __syncthreads();
       PageSrc nps;
-      nps.load = false;
+      nps.load = 0;
       if (has_next) {
         if (nseg == seg) {
-          nps = nblk == pre_blk ? page_src_id(L, nblk, pre_id) : page_src(nseg, L, nblk);
-          bad_block = bad_block || !nps.load;
+          // every page but the segment's last is full; its block number was prefetched
+          nps = nblk == pre_blk ? page_src_id(nblk + 1 == nb ? last_rows : kPage, pre_id)
+                                : page_src(nseg, L, nblk);
+          bad_block = bad_block || nps.load == 0;
         } else {
           nps = page_src(nseg, sload(segt + (size_t)nseg * kSegWords + S_SEQLEN), nblk);
-          bad_block_next = bad_block_next || !nps.load;
+          bad_block_next = bad_block_next || nps.load == 0;
         }
       }
       const uint32_t next_lds = lds0 + (buf ^ 1) * kBufBytes;
