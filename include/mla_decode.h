@@ -95,8 +95,12 @@ int mla_plan_size(int batch, int s_q, int num_heads, int num_workgroups,
  * mla_plan_size): the concatenated stream of 64-token blocks of every
  * (sequence, 128-row group) is cut into near-equal contiguous ranges, one per
  * workgroup; a sequence cut at a range boundary is computed in parts and
- * merged by log-sum-exp.  min_split_blocks (0 = library default of 8) is the
- * smallest range a workgroup is given, which bounds the number of parts.
+ * merged by log-sum-exp.  The stream of T blocks is cut into n ranges:
+ * n = T / min_split_blocks for min_split_blocks > 0 (the smallest range a
+ * workgroup is given, which bounds the number of parts), or by default
+ * (min_split_blocks = 0) the fewest ranges whose longest is as short as with
+ * one range per workgroup, n = ceil(T / ceil(T / num_workgroups)); always
+ * 1 <= n <= min(T, num_workgroups).
  * The plan is reusable by every mla_decode_fwd with the same sizes and
  * seqlens (e.g. all layers of one decode step).
  */

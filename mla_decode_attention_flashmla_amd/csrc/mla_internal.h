@@ -10,7 +10,6 @@ constexpr int kPage = 64;        // tokens per KV block
 constexpr int kDqk = 576;        // latent 512 + rope 64
 constexpr int kDv = 512;         // V = first 512 columns
 constexpr int kGroupRows = 128;  // query rows (t, h) per row group, one workgroup's rows
-constexpr int kDefaultMinSplitBlocks = 8;
 
 // Scheduling metadata, int32 words.
 //   header      kHdrWords

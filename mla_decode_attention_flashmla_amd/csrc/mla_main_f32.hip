@@ -89,32 +89,56 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
       for (int r = 0; r < kRows; ++r) acc[r][0] = acc[r][1] = 0.f;
       __syncthreads();
 
-      for (int tok0 = tok_begin; tok0 < tok_end; tok0 += kTok) {
-        // keys tok0 .. tok0+31 -> LDS; rows at or past the length are zero
-        for (int i = tid; i < kTok * kDqk; i += kThreads) {
-          const int j = i / kDqk, d = i - j * kDqk;
-          const int tok = tok0 + j;
-          float v = 0.f;
-          if (tok < tok_end) {
-            const int id = block_table[(size_t)b * max_blocks + tok / kPage];
-            if (id >= 0 && (int64_t)id < num_blocks) {
-              v = kv[((size_t)id * kPage + (tok % kPage)) * kDqk + d];
-            } else {
-              bad_s = 1;
-            }
-          }
-          ks[j * kLd + d] = v;
+      // Keys of a 32-token tile, read into registers one tile ahead (18 float4 per
+      // thread, all in flight at once).  A tile starts on a multiple of 32 tokens, so it
+      // lies in one block: one block number, then 32 consecutive rows of it, one
+      // contiguous run.  Rows at or past the length are zero.
+      constexpr int kVec = kTok * kDqk / 4 / kThreads;
+      static_assert(kVec * 4 * kThreads == kTok * kDqk, "tile split");
+      float4 kreg[kVec];
+      auto load_tile = [&](int t0) {
+        const int id = block_table[(size_t)b * max_blocks + t0 / kPage];
+        const bool ok = id >= 0 && (int64_t)id < num_blocks;
+        if (!ok && tid == 0) bad_s = 1;
+        const float4* src =
+            (const float4*)(kv + ((size_t)(ok ? id : 0) * kPage + (t0 % kPage)) * kDqk);
+        const int n_in = ok ? min(kTok, tok_end - t0) * kDqk / 4 : 0;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          const int i = tid + kThreads * k;
+          kreg[k] = i < n_in ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+      };
+      if (tok_begin < tok_end) load_tile(tok_begin);
+      for (int tok0 = tok_begin; tok0 < tok_end; tok0 += kTok) {
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          const int i = 4 * (tid + kThreads * k);
+          const int j = i / kDqk, d = i - j * kDqk;
+          float* dst = ks + j * kLd + d;
+          dst[0] = kreg[k].x;
+          dst[1] = kreg[k].y;
+          dst[2] = kreg[k].z;
+          dst[3] = kreg[k].w;
+        }
+        if (tok0 + kTok < tok_end) load_tile(tok0 + kTok);
         __syncthreads();
         // scores: thread -> key j, rows r and r + 8
         {
+          // four independent partial sums per row keep the LDS reads and FMAs pipelined
           const int j = tid & 31, r = tid >> 5;
-          float s0 = 0.f, s1 = 0.f;
-          for (int d = 0; d < kDqk; ++d) {
-            const float kd = ks[j * kLd + d];
-            s0 = fmaf(qs[r * kLd + d], kd, s0);
-            s1 = fmaf(qs[(r + 8) * kLd + d], kd, s1);
+          float a0[4] = {0.f, 0.f, 0.f, 0.f}, a1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+          for (int d = 0; d < kDqk; d += 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float kd = ks[j * kLd + d + e];
+              a0[e] = fmaf(qs[r * kLd + d + e], kd, a0[e]);
+              a1[e] = fmaf(qs[(r + 8) * kLd + d + e], kd, a1[e]);
+            }
           }
+          const float s0 = (a0[0] + a0[1]) + (a0[2] + a0[3]);
+          const float s1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
           const int tok = tok0 + j;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {

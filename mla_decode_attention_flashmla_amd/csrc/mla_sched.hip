@@ -117,9 +117,20 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
   }
   __syncthreads();
 
-  // 3. cut the stream into n items, spread over the slots
-  const int64_t minb = min_split_blocks > 0 ? min_split_blocks : kDefaultMinSplitBlocks;
-  int64_t n = floordiv(T, minb);
+  // 3. cut the stream into n items, spread over the slots.  By default n is the fewest
+  // items whose largest one is as short as with one item per slot, n = ceil(T / c) with
+  // c = ceil(T / slots) blocks per item: the same critical path with fewer split parts
+  // (each part costs a partial result written and read back).  A caller-given
+  // min_split_blocks sets n = T / min_split_blocks instead.  Either way
+  // 1 <= n <= min(T, slots).
+  int64_t n;
+  if (min_split_blocks > 0) {
+    n = floordiv(T, min_split_blocks);
+  } else {
+    const int64_t c = floordiv(T + num_wg - 1, num_wg);
+    n = c > 0 ? floordiv(T + c - 1, c) : 1;
+  }
+  if (n > T) n = T;
   if (n < 1) n = 1;
   if (n > num_wg) n = num_wg;
   // the plan stores block offsets in 32 bits: a longer stream gets no work and a status bit
