@@ -15,7 +15,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = 16;        // rows per slice
 constexpr int kTok = 32;         // keys per LDS tile
-constexpr int kLd = kDqk + 1;    // padded LDS row (fp32 words)
+constexpr int kLd = kDqk + 4;    // padded LDS row (fp32 words): 16-byte rows, rows j and
+                                 // j+1 four banks apart for 16-byte reads
 
 __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kv, int64_t num_blocks,
@@ -23,8 +24,8 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
     int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ meta, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
-  __shared__ float qs[kRows * kLd];
-  __shared__ float ks[kTok * kLd];
+  __shared__ __attribute__((aligned(16))) float qs[kRows * kLd];
+  __shared__ __attribute__((aligned(16))) float ks[kTok * kLd];
   __shared__ float ps[kRows * kTok];
   __shared__ float alpha_s[kRows], m_s[kRows], l_s[kRows];
   __shared__ int bad_s;
@@ -71,16 +72,26 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
     const int tok_begin = kb * kPage, tok_end = min(ke * kPage, L);
 
     for (int r0 = 0; r0 < rows_in_group; r0 += kRows) {
-      // Q slice -> LDS (rows past M are zero)
-      for (int i = tid; i < kRows * kDqk; i += kThreads) {
-        const int r = i / kDqk, d = i - r * kDqk;
-        const int row = rg * kGroupRows + r0 + r;
-        float v = 0.f;
-        if (r0 + r < rows_in_group) {
-          const int t = row / heads, hd = row - t * heads;
-          v = q[(((size_t)b * s_q + t) * heads + hd) * kDqk + d];
+      // Q slice -> LDS (rows past M are zero).  Row (t, h) of sequence b is q row
+      // b*M + t*heads + h, so the slice's rows are one contiguous run.
+      {
+        const float4* qsrc =
+            (const float4*)(q + ((size_t)b * M + rg * kGroupRows + r0) * kDqk);
+        const int n_in = min(kRows, rows_in_group - r0) * kDqk / 4;
+        constexpr int kQVec = kRows * kDqk / 4 / kThreads;
+        static_assert(kQVec * 4 * kThreads == kRows * kDqk, "slice split");
+        float4 qv[kQVec];
+#pragma unroll
+        for (int k = 0; k < kQVec; ++k) {
+          const int i = tid + kThreads * k;
+          qv[k] = i < n_in ? qsrc[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        qs[r * kLd + d] = v;
+#pragma unroll
+        for (int k = 0; k < kQVec; ++k) {
+          const int i = 4 * (tid + kThreads * k);
+          const int r = i / kDqk, d = i - r * kDqk;
+          *(float4*)(qs + r * kLd + d) = qv[k];
+        }
       }
       if (tid < kRows) { m_s[tid] = -INFINITY; l_s[tid] = 0.f; }
       if (tid == 0) bad_s = 0;
@@ -115,11 +126,7 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
         for (int k = 0; k < kVec; ++k) {
           const int i = 4 * (tid + kThreads * k);
           const int j = i / kDqk, d = i - j * kDqk;
-          float* dst = ks + j * kLd + d;
-          dst[0] = kreg[k].x;
-          dst[1] = kreg[k].y;
-          dst[2] = kreg[k].z;
-          dst[3] = kreg[k].w;
+          *(float4*)(ks + j * kLd + d) = kreg[k];
         }
         if (tok0 + kTok < tok_end) load_tile(tok0 + kTok);
         __syncthreads();
@@ -130,15 +137,22 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
           float a0[4] = {0.f, 0.f, 0.f, 0.f}, a1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
           for (int d = 0; d < kDqk; d += 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float kd = ks[j * kLd + d + e];
-              a0[e] = fmaf(qs[r * kLd + d + e], kd, a0[e]);
-              a1[e] = fmaf(qs[(r + 8) * kLd + d + e], kd, a1[e]);
-            }
+            const float4 k4 = *(const float4*)(ks + j * kLd + d);
+            const float4 x4 = *(const float4*)(qs + r * kLd + d);
+            const float4 y4 = *(const float4*)(qs + (r + 8) * kLd + d);
+            a0[0] = fmaf(x4.x, k4.x, a0[0]);
+            a0[1] = fmaf(x4.y, k4.y, a0[1]);
+            a0[2] = fmaf(x4.z, k4.z, a0[2]);
+            a0[3] = fmaf(x4.w, k4.w, a0[3]);
+            a1[0] = fmaf(y4.x, k4.x, a1[0]);
+            a1[1] = fmaf(y4.y, k4.y, a1[1]);
+            a1[2] = fmaf(y4.z, k4.z, a1[2]);
+            a1[3] = fmaf(y4.w, k4.w, a1[3]);
           }
           const float s0 = (a0[0] + a0[1]) + (a0[2] + a0[3]);
           const float s1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
+          // online softmax: a row's 32 keys sit in 32 consecutive lanes of one wave, so
+          // its max and sum are shuffle reductions over those lanes
           const int tok = tok0 + j;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
@@ -146,31 +160,27 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
             const int row = rg * kGroupRows + r0 + rr;
             const int t = row / heads;
             const int n = causal ? L - s_q + 1 + t : L;
-            const float sv = (u ? s1 : s0) * scale;
-            ps[rr * kTok + j] = (tok < n && tok < tok_end) ? sv : -INFINITY;
-          }
-        }
-        __syncthreads();
-        // online softmax, one thread per row
-        if (tid < kRows) {
-          const float m_old = m_s[tid];
-          float mx = -INFINITY;
-          for (int j = 0; j < kTok; ++j) mx = fmaxf(mx, ps[tid * kTok + j]);
-          const float m_new = fmaxf(m_old, mx);
-          float alpha = 1.f, sum = 0.f;
-          if (m_new != -INFINITY) {
-            alpha = m_old == -INFINITY ? 0.f : expf(m_old - m_new);
-            for (int j = 0; j < kTok; ++j) {
-              const float p = expf(ps[tid * kTok + j] - m_new);
-              ps[tid * kTok + j] = p;
-              sum += p;
+            const float sv = (tok < n && tok < tok_end) ? (u ? s1 : s0) * scale : -INFINITY;
+            float mx = sv;
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+            const float m_old = m_s[rr];
+            const float m_new = fmaxf(m_old, mx);
+            float alpha = 1.f, p = 0.f;
+            if (m_new != -INFINITY) {
+              alpha = m_old == -INFINITY ? 0.f : expf(m_old - m_new);
+              p = expf(sv - m_new);
             }
-          } else {
-            for (int j = 0; j < kTok; ++j) ps[tid * kTok + j] = 0.f;
+            float sum = p;
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 32);
+            ps[rr * kTok + j] = p;
+            if (j == 0) {
+              m_s[rr] = m_new;
+              l_s[rr] = l_s[rr] * alpha + sum;
+              alpha_s[rr] = alpha;
+            }
           }
-          m_s[tid] = m_new;
-          l_s[tid] = l_s[tid] * alpha + sum;
-          alpha_s[tid] = alpha;
         }
         __syncthreads();
         // O += P . V, thread -> columns 2*tid, 2*tid+1
@@ -182,8 +192,9 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
             float o0 = acc[r][0] * a, o1 = acc[r][1] * a;
             for (int j = 0; j < kTok; ++j) {
               const float p = ps[r * kTok + j];
-              o0 = fmaf(p, ks[j * kLd + c], o0);
-              o1 = fmaf(p, ks[j * kLd + c + 1], o1);
+              const float2 v2 = *(const float2*)(ks + j * kLd + c);
+              o0 = fmaf(p, v2.x, o0);
+              o1 = fmaf(p, v2.y, o1);
             }
             acc[r][0] = o0;
             acc[r][1] = o1;
