@@ -96,8 +96,10 @@ def cpu_baseline(d, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    # ~0.1 s of warm-up: the GPU needs tens of milliseconds of load to reach its
+    # steady clocks (100 steps after 20 warm-up steps ran ~12% slower than steady state)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="gate_b64_l8192")
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--min-split-blocks", type=int, default=0)
