@@ -25,9 +25,10 @@
 // rescale, read-out); the compiler works in VGPRs only (Q fragments, scores,
 // P, LDS fragments).  The score MFMAs are asm too, to keep their accumulators
 // in VGPRs.  Wait states the hardware needs around these MFMAs are written
-// into the asm: after the last score MFMA and the last PV MFMA of a page (before
-// VALU or AGPR reads of their results) and before the first PV MFMA (after VALU
-// writes of P and O).
+// into the asm: after the last score MFMA of a page (before VALU reads of the
+// scores), before the first PV MFMA (after VALU writes of P and O), and before
+// the epilogue reads O^T (a rescale reads it only after the next page's score
+// MFMAs, so the PV loop ends without them).
 //
 // The running max is allowed to lag the true row max by up to 8 (log2 units):
 // O is only rescaled when a page raises some row's max by more than that, so
@@ -151,18 +152,6 @@ __device__ __forceinline__ void o_pv(int ct, const bf16x8& a, const bf16x8& b) {
   case n:                                                                                     \
     asm volatile("v_mfma_f32_32x32x16_bf16 " MLA_OT##n ", %0, %1, " MLA_OT##n ::"v"(a), "v"(b) \
                  : MLA_OT##n##_CLOBBER);                                                      \
-    break;
-    MLA_FOR_TILES(X)
-#undef X
-  }
-}
-// last PV MFMA of a page: wait states before any VALU/AGPR read of O^T
-__device__ __forceinline__ void o_pv_last(int ct, const bf16x8& a, const bf16x8& b) {
-  switch (ct) {
-#define X(n)                                                                             \
-  case n:                                                                                \
-    asm volatile("v_mfma_f32_32x32x16_bf16 " MLA_OT##n ", %0, %1, " MLA_OT##n "\n\t"     \
-                 "s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"v"(a), "v"(b) : MLA_OT##n##_CLOBBER); \
     break;
     MLA_FOR_TILES(X)
 #undef X
@@ -545,11 +534,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         constexpr int i = decltype(I)::value;
         constexpr int kc = i / kCTiles, ct = i % kCTiles;
         if constexpr (i + kVDepth < kPv) vf[(i + kVDepth) % (kVDepth + 1)] = vfrag(i + kVDepth);
-        if constexpr (i + 1 < kPv) {
-          o_pv(ct, vf[i % (kVDepth + 1)], pf[kc]);
-        } else {
-          o_pv_last(ct, vf[i % (kVDepth + 1)], pf[kc]);
-        }
+        // no wait states after the page's last PV MFMA: O^T is next read by VALU or
+        // AGPR moves only at a rescale (after the next page's score MFMAs) or in the
+        // epilogue, which waits for it
+        o_pv(ct, vf[i % (kVDepth + 1)], pf[kc]);
         __builtin_amdgcn_sched_barrier(0);
       };
       static_for<0, kPv>(pv_step);
@@ -557,6 +545,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     }
 
     // ---- epilogue: this segment's rows, whole or as one part ----
+    // wait states for the last PV MFMA's O^T before it is read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     const bool bad = bad_block || mismatch;
     if (wave_active) {
       const int nsplit = sload(segt + (size_t)seg * kSegWords + S_NSPLIT);
