@@ -204,6 +204,98 @@ def make_workload(w: Workload, seqlens: Optional[np.ndarray] = None, guard_block
     }
 
 
+@dataclasses.dataclass(frozen=True)
+class SparseWorkload:
+    """Shape and distribution of one synthetic sparse MLA decode workload (s_q = 1).
+
+    Each sequence of ``context`` tokens lists ``topk`` selected token positions,
+    distinct and in random order; a sequence shorter than ``topk`` lists all of its
+    positions and pads with -1.  With ``pool_blocks`` the block table draws its
+    entries from a pool of that many blocks (with replacement), so a long logical
+    context fits a small pool while the rows read stay scattered; without it every
+    block of every sequence is its own.
+    """
+
+    name: str
+    batch: int
+    heads: int
+    context: int
+    topk: int
+    pool_blocks: int = 0
+    scale_denominator: int = 192
+    sigma: float = 0.5
+    ragged: bool = False
+    seed: int = 0
+
+    @property
+    def scale(self) -> np.float32:
+        return np.float32(float(self.scale_denominator) ** -0.5)
+
+
+SPARSE_WORKLOADS = {
+    # 128K context, 2048 selected tokens per sequence, 64 sequences
+    "sparse_b64_l131072_topk2048": SparseWorkload("sparse_b64_l131072_topk2048", 64, 128,
+                                                  131072, 2048, pool_blocks=8192, seed=6),
+}
+
+
+def make_sparse_workload(w: SparseWorkload, seqlens: Optional[np.ndarray] = None,
+                         pad: int = 0) -> dict:
+    """Draw one sparse workload: the paged-decode arrays of ``make_workload`` plus
+    ``indices`` [B, topk] int32.  ``pad`` extra -1 entries (and as many positions at or
+    past the length) replace list entries, to exercise padding."""
+    streams = np.random.SeedSequence(w.seed).spawn(6)
+    rng_len = np.random.Generator(np.random.PCG64(streams[0]))
+    rng_tab = np.random.Generator(np.random.PCG64(streams[1]))
+    rng_idx = np.random.Generator(np.random.PCG64(streams[4]))
+    if seqlens is not None:
+        lens = np.asarray(seqlens, dtype=np.int32).copy()
+    elif w.ragged:
+        lens = rng_len.integers(1, w.context, size=w.batch, endpoint=True).astype(np.int32)
+    else:
+        lens = np.full(w.batch, w.context, dtype=np.int32)
+    B = int(lens.shape[0])
+    nblk = (lens.astype(np.int64) + PAGE - 1) // PAGE
+    max_blocks = max(1, int(nblk.max()) if B else 1)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    if w.pool_blocks:
+        num_blocks = w.pool_blocks
+        for b in range(B):
+            table[b, :nblk[b]] = rng_tab.integers(0, num_blocks, size=int(nblk[b]))
+    else:
+        num_blocks = int(nblk.sum())
+        perm = rng_tab.permutation(num_blocks).astype(np.int32)
+        off = 0
+        for b in range(B):
+            k = int(nblk[b])
+            table[b, :k] = perm[off:off + k]
+            off += k
+    idx = np.full((B, w.topk), -1, dtype=np.int32)
+    for b in range(B):
+        L = int(lens[b])
+        k = min(w.topk, L)
+        if k:
+            idx[b, :k] = rng_idx.choice(L, size=k, replace=False)
+        if pad:
+            slots = rng_idx.choice(w.topk, size=min(pad, w.topk), replace=False)
+            half = len(slots) // 2
+            idx[b, slots[:half]] = -1
+            idx[b, slots[half:]] = L + rng_idx.integers(0, 1000, size=len(slots) - half)
+        idx[b] = idx[b, rng_idx.permutation(w.topk)]
+    q = _normal_fill(streams[2], B * w.heads * D_QK, w.sigma, True).reshape(B, 1, w.heads, D_QK)
+    kv = _normal_fill(streams[3], num_blocks * PAGE * D_QK, w.sigma, True)
+    kv = kv.reshape(num_blocks, PAGE, D_QK)
+    return {
+        "workload": w,
+        "q": q,
+        "kv_cache": kv,
+        "block_table": table,
+        "seqlens": lens,
+        "indices": idx,
+        "scale": w.scale,
+    }
+
+
 def sample_sequences(batch: int, count: int, seed: int) -> np.ndarray:
     """Indices of sequences checked one by one at full size: first, last and a seeded draw."""
     rng = np.random.default_rng(seed + 1000)

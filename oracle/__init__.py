@@ -5,5 +5,6 @@ by the product path.  It shares no code with the HIP kernels.
 """
 from .mla_oracle import (  # noqa: F401
     PAGE, D_QK, D_V, widen, visible_keys, gather_rows, check_lengths, attend_one,
-    mla_decode, softmax_weights, merge_partials, brute_force,
+    mla_decode, softmax_weights, merge_partials, brute_force, selected_rows,
+    mla_decode_sparse,
 )

@@ -119,6 +119,55 @@ def mla_decode(q, kv_cache, block_table, seqlens, scale, causal=False, dtype="bf
     return out, lse
 
 
+def selected_rows(kv_cache: np.ndarray, block_table: np.ndarray, b: int, seqlen: int,
+                  positions: np.ndarray) -> np.ndarray:
+    """Rows of sequence b at the listed token positions, in list order.
+
+    Positions outside [0, seqlen) select nothing; a position listed twice is a key twice.
+    """
+    pos = np.asarray(positions, dtype=np.int64)
+    pos = pos[(pos >= 0) & (pos < seqlen)]
+    rows = np.empty((pos.shape[0], kv_cache.shape[-1]), dtype=kv_cache.dtype)
+    for k, p in enumerate(pos.tolist()):
+        blk = int(block_table[b, p // PAGE])
+        if blk < 0 or blk >= kv_cache.shape[0]:
+            raise ValueError(f"sequence {b}: block table entry outside the pool")
+        rows[k] = kv_cache[blk, p % PAGE]
+    return rows
+
+
+def mla_decode_sparse(q, kv_cache, block_table, seqlens, indices, scale, dtype="bf16",
+                      batches: Iterable[int] | None = None):
+    """Float64 O [B, s_q, H, 512] and LSE [B, s_q, H] of sparse MLA decode.
+
+    The SparseMLA variant of the Triton-TLE talk's performance section (a 128K
+    context of which each query reads a selected subset of tokens): every query of
+    sequence b attends to the keys at the token positions ``indices[b, :]`` (the
+    selected subset, e.g. a top-k list), with the same scores, softmax and outputs
+    as ``mla_decode`` over just those keys.  Positions outside [0, L_b) are padding
+    and select nothing; a position listed twice counts twice.  No selected key
+    gives O = 0 and LSE = -inf.
+    """
+    q = np.asarray(q)
+    B, s_q, H, D = q.shape
+    if D != D_QK or kv_cache.shape[1:] != (PAGE, D_QK):
+        raise ValueError("expected q [B,s_q,H,576] and kv_cache [blocks,64,576]")
+    seqlens = np.asarray(seqlens)
+    check_lengths(seqlens, block_table, s_q, False)
+    indices = np.asarray(indices)
+    if indices.ndim != 2 or indices.shape[0] != B:
+        raise ValueError("expected indices [B, topk]")
+    scale = float(scale)
+    out = np.full((B, s_q, H, D_V), np.nan)
+    lse = np.full((B, s_q, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        keys = widen(selected_rows(kv_cache, block_table, b, int(seqlens[b]), indices[b]), dtype)
+        qb = widen(q[b], dtype)
+        for t in range(s_q):
+            out[b, t], lse[b, t] = attend_one(qb[t], keys, scale)
+    return out, lse
+
+
 def softmax_weights(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
     """The attention weights p[h, j] = exp(s_j - LSE_h) the outputs are built from."""
     s = scale * (q_rows @ keys.T)

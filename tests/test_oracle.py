@@ -287,3 +287,81 @@ def test_bf16_widening_is_exact():
     assert vals[0] == 1.0 and vals[1] == -2.0 and vals[3] == 0.0
     assert vals[2] == 0.333984375           # 0x3EAB = 1.0101011b * 2^-2
     assert vals[4] == 3.3895313892515355e38  # largest finite bf16
+
+
+# ---------------------------------------------------------------- sparse variant
+
+
+def _sparse_case(L=300, topk=128, pad=0, seed=7):
+    w = I.SparseWorkload("t", 3, 16, L, topk, seed=seed)
+    return I.make_sparse_workload(w, pad=pad)
+
+
+def test_sparse_full_list_equals_dense():
+    """Listing every position of a sequence (in any order, padded) selects its whole
+    context: the sparse result is the dense one (the gather goes through the same block
+    table, so a wrong position-to-row map fails here)."""
+    d = _sparse_case(L=100, topk=128)
+    ref_o, ref_l = O.mla_decode(d["q"], d["kv_cache"], d["block_table"], d["seqlens"],
+                                d["scale"])
+    o, l = O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"],
+                               d["indices"], d["scale"])
+    assert (d["indices"] == -1).sum() == 3 * 28
+    np.testing.assert_allclose(o, ref_o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l, ref_l, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_order_and_padding_do_not_matter():
+    d = _sparse_case(L=500, topk=128, pad=20)
+    idx = d["indices"]
+    o1, l1 = O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], idx,
+                                 d["scale"])
+    # the same selections, reordered, with the padding squeezed out and re-added
+    rng = np.random.default_rng(3)
+    idx2 = np.full((3, 200), -1, dtype=np.int32)
+    for b in range(3):
+        keep = idx[b][(idx[b] >= 0) & (idx[b] < d["seqlens"][b])]
+        idx2[b, :keep.size] = rng.permutation(keep)
+    o2, l2 = O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], idx2,
+                                 d["scale"])
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_duplicate_position_counts_twice():
+    """Two copies of one key: the weights are 1/2 each, so O is that key's V row and
+    LSE is its score plus ln 2 (the single-key result from the dense definition)."""
+    d = _sparse_case(L=300, topk=128)
+    j = 77
+    idx = np.full((3, 128), -1, dtype=np.int32)
+    idx[:, 5] = j
+    idx[:, 90] = j
+    o, l = O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], idx,
+                               d["scale"])
+    one = np.full_like(idx, -1)
+    one[:, 0] = j
+    o1, l1 = O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], one,
+                                 d["scale"])
+    row = O.widen(d["kv_cache"][d["block_table"][1, j // 64], j % 64, :512], "bf16")
+    np.testing.assert_allclose(o1[1, 0], np.broadcast_to(row, (16, 512)), rtol=1e-15)
+    np.testing.assert_allclose(o, o1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l, l1 + math.log(2.0), rtol=1e-12)
+
+
+def test_sparse_nothing_selected_and_brute_force():
+    d = _sparse_case(L=40, topk=64)
+    idx = np.full((3, 64), -1, dtype=np.int32)
+    idx[1, :3] = [40, 41, 1000]                     # at or past the length: padding too
+    o, l = O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], idx,
+                               d["scale"])
+    assert np.all(o == 0) and np.all(l == -np.inf)
+    # a few selections against pure-Python loops over the selected rows
+    idx[2, :4] = [3, 39, 0, 17]
+    o, l = O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], idx,
+                               d["scale"], batches=[2])
+    kv = O.widen(d["kv_cache"], "bf16")
+    rows = [list(kv[d["block_table"][2, p // 64], p % 64]) for p in (3, 39, 0, 17)]
+    qs = [[list(O.widen(d["q"][2, 0, h], "bf16")) for h in range(2)]]
+    bo, bl = O.brute_force([qs], [rows], float(d["scale"]), False, 1)
+    np.testing.assert_allclose(o[2, 0, :2], np.array(bo[0][0]), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l[2, 0, :2], np.array(bl[0][0]), rtol=1e-12)
