@@ -150,6 +150,41 @@ int mla_decode_combine(int dtype, const void* q, const void* kv_cache, int64_t n
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Sparse MLA decode: the SparseMLA variant of the Triton-TLE talk's performance
+ * section, in which each query reads only a selected list of token positions out of a
+ * long (128K) context.  For every sequence b and head h (one query token, s_q = 1):
+ *
+ *   sel_b   = [ indices[b][k] for k < topk  if 0 <= indices[b][k] < L_b ]
+ *             (other entries, e.g. -1, are padding; a position listed twice counts twice)
+ *   s_j     = scale * sum_d q[b][0][h][d] * R_b[j][d]        (j in sel_b)
+ *   lse     = ln sum_j exp(s_j),   out[c] = sum_j exp(s_j - lse) * R_b[j][c]
+ *
+ * with R_b the rows of sequence b through its block table, as in mla_decode_fwd.  No
+ * selected key gives out = 0 and lse = -inf.
+ *
+ * Layouts as in mla_decode_fwd with s_q = 1 and dtype bf16; in addition
+ *   indices   [batch][topk] int32 (device), token positions within each sequence.
+ * topk is a positive multiple of 64, at most 65536; num_blocks at most 2^25.
+ *
+ * One call enqueues, on `stream`: the packing of the selected rows (one kernel picks
+ * and orders them, one copies them into workspace blocks), the split scheduler over
+ * the packed lengths (it writes `meta`, so no separate mla_get_split_metadata call
+ * is made), the main kernel and the combine.  meta/workspace: device buffers of at
+ * least the sizes mla_sparse_plan_size returns for the same batch, num_heads, topk and
+ * num_workgroups.  Errors and device status bits as for mla_decode_fwd (a selected
+ * position whose block number is outside the pool: MLA_STATUS_BAD_BLOCK and NaN for
+ * that sequence; an invalid length: MLA_STATUS_BAD_SEQLEN and NaN).
+ */
+int mla_sparse_plan_size(int batch, int num_heads, int topk, int num_workgroups,
+                         size_t* meta_bytes, size_t* workspace_bytes);
+int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_blocks,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seqlens, const int32_t* indices, int topk,
+                          int batch, int num_heads, float scale, float* out, float* lse,
+                          int32_t* meta, size_t meta_bytes, int num_workgroups,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Synchronizes `stream`, then copies the plan's device status word
  * (MLA_STATUS_* bits, 0 = clean) into *status (host pointer).
  */

@@ -31,8 +31,8 @@ D_QK = 576
 D_V = 512
 
 EXPORTS = ("mla_device_workgroups", "mla_plan_size", "mla_get_split_metadata",
-           "mla_decode_fwd", "mla_decode_main", "mla_decode_combine", "mla_read_status",
-           "mla_status_string")
+           "mla_decode_fwd", "mla_decode_main", "mla_decode_combine", "mla_sparse_plan_size",
+           "mla_decode_sparse_fwd", "mla_read_status", "mla_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
                 c_p, c_p, c_sz, c_int, c_p, c_sz, c_p]
     for fn in ("mla_decode_fwd", "mla_decode_main", "mla_decode_combine"):
         getattr(lib, fn).argtypes = fwd_args
+    lib.mla_sparse_plan_size.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(c_sz),
+                                         ctypes.POINTER(c_sz)]
+    lib.mla_decode_sparse_fwd.argtypes = [c_p, c_p, c_i64, c_p, c_int, c_p, c_p, c_int, c_int,
+                                          c_int, c_f, c_p, c_p, c_p, c_sz, c_int, c_p, c_sz, c_p]
     lib.mla_read_status.argtypes = [c_p, c_p, ctypes.POINTER(ctypes.c_int32)]
     lib.mla_status_string.argtypes = [c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -177,6 +181,50 @@ def decode_main(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream
 def decode_combine(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream=None):
     _decode("mla_decode_combine", q, kv_cache, block_table, seqlens, scale, out, lse, plan,
             stream)
+
+
+def sparse_plan_size(batch: int, heads: int, topk: int, num_workgroups: int) -> tuple[int, int]:
+    m, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mla_sparse_plan_size", load().mla_sparse_plan_size(
+        batch, heads, topk, num_workgroups, ctypes.byref(m), ctypes.byref(w)))
+    return m.value, w.value
+
+
+def alloc_sparse_plan(batch: int, heads: int, topk: int, num_workgroups: Optional[int] = None,
+                      device=None) -> Plan:
+    """Allocate (with torch) the metadata and workspace buffers of sparse decode."""
+    import torch
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    if num_workgroups is None:
+        num_workgroups = device_workgroups(device.index or 0)
+    mb, wb = sparse_plan_size(batch, heads, topk, num_workgroups)
+    meta = torch.empty(mb // 4, dtype=torch.int32, device=device)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=device)
+    return Plan(meta, ws, batch, 1, heads, 0, topk // PAGE, num_workgroups)
+
+
+def decode_sparse_fwd(q, kv_cache, block_table, seqlens, indices, scale, out, lse, plan: Plan,
+                      stream=None) -> None:
+    """mla_decode_sparse_fwd: packing of the selected rows, scheduler, main kernel and
+    combine into out [B,1,H,512] and lse [B,1,H]."""
+    lib = load()
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seqlens", seqlens), ("indices", indices), ("out", out), ("lse", lse)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, s_q, H, D = q.shape
+    topk = indices.shape[1]
+    if (D != D_QK or s_q != 1 or kv_cache.shape[1:] != (PAGE, D_QK) or block_table.shape[0] != B
+            or indices.shape[0] != B or tuple(out.shape) != (B, 1, H, D_V)
+            or tuple(lse.shape) != (B, 1, H) or kv_cache.dtype != q.dtype
+            or _dtype_code(q) != MLA_DTYPE_BF16):
+        raise ValueError("shape/dtype mismatch with bf16 q [B,1,H,576], kv [n,64,576], "
+                         "indices [B,topk]")
+    _check("mla_decode_sparse_fwd", lib.mla_decode_sparse_fwd(
+        q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(),
+        block_table.shape[1], seqlens.data_ptr(), indices.data_ptr(), topk, B, H, float(scale),
+        out.data_ptr(), lse.data_ptr(), plan.meta.data_ptr(), plan.meta.numel() * 4,
+        plan.num_workgroups, plan.workspace.data_ptr(), plan.workspace.numel(), _stream(stream)))
 
 
 def read_status(plan: Plan, stream=None) -> int:

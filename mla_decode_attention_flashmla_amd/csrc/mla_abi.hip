@@ -154,6 +154,75 @@ int mla_read_status(const int32_t* meta, void* stream, int32_t* status) {
   return MLA_OK;
 }
 
+int mla_sparse_plan_size(int batch, int num_heads, int topk, int num_workgroups,
+                         size_t* meta_bytes, size_t* workspace_bytes) {
+  if (!meta_bytes || !workspace_bytes) return MLA_ERR_INVALID_ARG;
+  int rc = check_sizes(batch, 1, num_heads, num_workgroups);
+  if (rc) return rc;
+  if (topk < kPage || topk % kPage != 0) return MLA_ERR_INVALID_ARG;
+  if (topk > kMaxSparseTopk) return MLA_ERR_UNSUPPORTED;
+  *meta_bytes = meta_words(batch, 1, num_heads, num_workgroups) * sizeof(int32_t);
+  *workspace_bytes = align256(mla::workspace_bytes(batch, 1, num_heads, num_workgroups)) +
+                     sparse_scratch_bytes(batch, topk);
+  return MLA_OK;
+}
+
+int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_blocks,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seqlens, const int32_t* indices, int topk, int batch,
+                          int num_heads, float scale, float* out, float* lse, int32_t* meta,
+                          size_t meta_bytes, int num_workgroups, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  size_t need_meta = 0, need_ws = 0;
+  int rc = mla_sparse_plan_size(batch, num_heads, topk, num_workgroups, &need_meta, &need_ws);
+  if (rc) return rc;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  // pool rows are addressed with 32-bit row numbers
+  if (num_blocks < 0 || num_blocks > ((int64_t)1 << 25) || max_blocks_per_seq < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!meta) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!q || !out || !lse || !seqlens || !block_table || !indices) return MLA_ERR_INVALID_ARG;
+  if (num_blocks > 0 && !kv_cache) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (kv_cache && !aligned16(kv_cache)))
+    return MLA_ERR_INVALID_ARG;
+  if (meta_bytes < need_meta || workspace_bytes < need_ws) return MLA_ERR_PLAN;
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARG;
+
+  hipStream_t st = (hipStream_t)stream;
+  const size_t dense_ws = align256(mla::workspace_bytes(batch, 1, num_heads, num_workgroups));
+  const SparseScratch sc = sparse_scratch((char*)workspace + dense_ws, batch, topk);
+  if (launch_sparse_pack(seqlens, block_table, max_blocks_per_seq, num_blocks, indices, topk,
+                         batch, kv_cache, sc, st) != hipSuccess)
+    return MLA_ERR_HIP;
+  const int chunks = topk / kPage;
+  if (launch_sched(sc.packed_len, batch, 1, num_heads, 0, chunks, num_workgroups, 0, meta,
+                   st) != hipSuccess)
+    return MLA_ERR_HIP;
+  Problem p;
+  p.q = q;
+  p.kv = sc.packed_kv;
+  p.num_blocks = (int64_t)batch * chunks;
+  p.block_table = sc.packed_table;
+  p.max_blocks = chunks;
+  p.seqlens = sc.packed_len;
+  p.batch = batch;
+  p.s_q = 1;
+  p.heads = num_heads;
+  p.causal = 0;
+  p.scale = scale;
+  p.out = out;
+  p.lse = lse;
+  p.meta = meta;
+  p.num_wg = num_workgroups;
+  const size_t slots = num_slots(batch, 1, num_heads, num_workgroups);
+  p.part_o = (float*)workspace;
+  p.part_lse = p.part_o + slots * kGroupRows * kDv;
+  if (launch_main_bf16(p, st) != hipSuccess) return MLA_ERR_HIP;
+  if (launch_combine(p, st) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_status_string(int code) {
   switch (code) {
     case MLA_OK: return "ok";

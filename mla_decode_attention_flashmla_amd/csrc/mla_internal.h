@@ -66,11 +66,45 @@ struct Problem {
   float* part_lse;  // [slots][128]
 };
 
+// Sparse decode scratch, carved from the caller's workspace after the partial results:
+// the packed rows [batch * topk][576] bf16, the pool row of each packed row, the packed
+// block table [batch][topk / 64] and the packed lengths [batch].
+constexpr int kMaxSparseTopk = 65536;
+constexpr int kMaxSparseChunks = kMaxSparseTopk / kPage;
+struct SparseScratch {
+  void* packed_kv;
+  int32_t* src_row;
+  int32_t* packed_table;
+  int32_t* packed_len;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t sparse_scratch_bytes(int batch, int topk) {
+  const size_t rows = (size_t)batch * topk;
+  return align256(rows * kDqk * 2) + align256(rows * 4) + align256(rows / kPage * 4) +
+         align256((size_t)batch * 4);
+}
+inline SparseScratch sparse_scratch(void* base, int batch, int topk) {
+  const size_t rows = (size_t)batch * topk;
+  char* p = (char*)base;
+  SparseScratch s;
+  s.packed_kv = p;
+  p += align256(rows * kDqk * 2);
+  s.src_row = (int32_t*)p;
+  p += align256(rows * 4);
+  s.packed_table = (int32_t*)p;
+  p += align256(rows / kPage * 4);
+  s.packed_len = (int32_t*)p;
+  return s;
+}
+
 hipError_t launch_sched(const int32_t* seqlens, int batch, int s_q, int heads, int causal,
                         int max_blocks, int num_wg, int min_split_blocks, int32_t* meta,
                         hipStream_t stream);
 hipError_t launch_main_bf16(const Problem& p, hipStream_t stream);
 hipError_t launch_main_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_combine(const Problem& p, hipStream_t stream);
+hipError_t launch_sparse_pack(const int32_t* seqlens, const int32_t* block_table, int max_blocks,
+                              int64_t num_blocks, const int32_t* indices, int topk, int batch,
+                              const void* kv, const SparseScratch& s, hipStream_t stream);
 
 }  // namespace mla

@@ -108,3 +108,42 @@ def test_status_read_rejects_null(lib):
     v = ctypes.c_int32(0)
     assert lib.mla_read_status(None, None, ctypes.byref(v)) == B.MLA_ERR_INVALID_ARG
     assert lib.mla_read_status(4096, None, None) == B.MLA_ERR_INVALID_ARG
+
+
+def test_sparse_plan_size(lib):
+    meta, ws = B.sparse_plan_size(64, 128, 2048, 256)
+    assert meta == (32 + 8 * 256 + 8 * 64) * 4
+    dense = (256 + 64) * 128 * 513 * 4
+    rows = 64 * 2048
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert ws == a256(dense) + a256(rows * 1152) + a256(rows * 4) + a256(rows // 64 * 4) + a256(64 * 4)
+    for topk, code in ((0, B.MLA_ERR_INVALID_ARG), (100, B.MLA_ERR_INVALID_ARG),
+                       (131072, B.MLA_ERR_UNSUPPORTED)):
+        with pytest.raises(B.MlaError) as e:
+            B.sparse_plan_size(2, 128, topk, 256)
+        assert e.value.code == code
+
+
+def _sparse(lib, **kw):
+    a = dict(q=4096, kv=8192, nblk=4, table=12288, maxb=4, lens=16384, idx=20480, topk=128,
+             batch=1, heads=16, scale=0.1, out=24576, lse=28672, meta=32768, meta_bytes=1 << 20,
+             nwg=8, ws=36864, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mla_decode_sparse_fwd(a["q"], a["kv"], a["nblk"], a["table"], a["maxb"], a["lens"],
+                                     a["idx"], a["topk"], a["batch"], a["heads"], a["scale"],
+                                     a["out"], a["lse"], a["meta"], a["meta_bytes"], a["nwg"],
+                                     a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_sparse_decode_rejects_bad_arguments_without_touching_hip(lib):
+    assert _sparse(lib, topk=100) == B.MLA_ERR_INVALID_ARG       # not a multiple of 64
+    assert _sparse(lib, topk=0) == B.MLA_ERR_INVALID_ARG
+    assert _sparse(lib, topk=1 << 17) == B.MLA_ERR_UNSUPPORTED
+    assert _sparse(lib, idx=None) == B.MLA_ERR_INVALID_ARG
+    assert _sparse(lib, q=4100) == B.MLA_ERR_INVALID_ARG
+    assert _sparse(lib, scale=0.0) == B.MLA_ERR_INVALID_ARG
+    assert _sparse(lib, nblk=(1 << 25) + 1) == B.MLA_ERR_INVALID_ARG
+    assert _sparse(lib, meta_bytes=16) == B.MLA_ERR_PLAN
+    assert _sparse(lib, ws_bytes=1024) == B.MLA_ERR_PLAN
+    assert _sparse(lib, heads=2048) == B.MLA_ERR_UNSUPPORTED
+    assert _sparse(lib, batch=0, q=None, out=None) == B.MLA_OK
