@@ -48,6 +48,122 @@ def algorithmic_work(d):
     return byt, kv, flops
 
 
+def sparse_algorithmic_work(d):
+    """Bytes and flops of sparse decode: each selected row read once (plus its block
+    number), Q, the index lists, O and LSE; 2 * H * 1088 flops per selected key."""
+    import numpy as np
+
+    w = d["workload"]
+    idx = d["indices"].astype(np.int64)
+    lens = d["seqlens"].astype(np.int64)[:, None]
+    sel = int(((idx >= 0) & (idx < lens)).sum())
+    B, H = w.batch, w.heads
+    kv = sel * 576 * 2
+    byt = kv + sel * 4 + idx.size * 4 + B * H * (576 * 2 + 512 * 4 + 4) + B * 4
+    return byt, kv, 2 * H * (576 + 512) * sel
+
+
+def run_sparse(args):
+    """The sparse decode step (packing, scheduler, main kernel, combine: one C-ABI call)."""
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_flashmla_amd import binding as B
+    from mla_decode_attention_flashmla_amd import inputs as I
+
+    w = I.SPARSE_WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = I.make_sparse_workload(w)
+    dev = torch.device("cuda", 0)
+    q = torch.from_numpy(d["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = torch.from_numpy(d["kv_cache"].view(np.int16)).view(torch.bfloat16).to(dev)
+    table = torch.from_numpy(d["block_table"]).to(dev)
+    lens = torch.from_numpy(d["seqlens"]).to(dev)
+    idx = torch.from_numpy(d["indices"]).to(dev)
+    Bn, H = w.batch, w.heads
+    out = torch.empty((Bn, 1, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((Bn, 1, H), dtype=torch.float32, device=dev)
+    nwg = args.num_workgroups or B.device_workgroups(0)
+    plan = B.alloc_sparse_plan(Bn, H, w.topk, nwg, dev)
+    scale = float(d["scale"])
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.decode_sparse_fwd(q, kv, table, lens, idx, scale, out, lse, plan)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if B.read_status(plan) != 0:
+        raise SystemExit("device status flagged an error")
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    byt, kv_bytes, flops = sparse_algorithmic_work(d)
+    t_roof = max(byt / HBM_PEAK, flops / MFMA_PEAK["bf16"])
+    step_s = ms_step * 1e-3
+    if byt / HBM_PEAK >= flops / MFMA_PEAK["bf16"]:
+        roof = {"bound": "hbm", "achieved": byt / step_s / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / step_s / 1e12,
+                "peak": MFMA_PEAK["bf16"] / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    # the selected rows are read by the packing kernels and the main kernel reads the
+    # packed copy, so the roofline is taken over the whole call
+    roof["kernel"] = "mla_decode_sparse_fwd (pack, scheduler, main, combine)"
+    roof["kernel_us"] = ms_step * 1e3
+    res = {
+        "metric": METRIC, "value": 100.0 * t_roof / step_s, "unit": "% of roofline",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": Bn, "s_q": 1, "heads": H,
+                   "seq_len": w.context, "topk": w.topk, "pool_blocks": w.pool_blocks,
+                   "block_size": 64, "head_dim": 576, "v_dim": 512, "num_workgroups": nwg,
+                   "parallelism": "single-gpu"},
+        "tflops": flops / step_s / 1e12, "kv_gbs": kv_bytes / step_s / 1e9,
+        "alg_bytes": byt, "alg_flops": flops, "roofline_us": t_roof * 1e6, "wall_s": wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import mla_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        done = []
+        c0 = time.perf_counter()
+        for b in range(Bn):
+            O.mla_decode_sparse(d["q"], d["kv_cache"], d["block_table"], d["seqlens"],
+                                d["indices"], scale, batches=[b])
+            done.append(b)
+            if time.perf_counter() - c0 >= args.cpu_budget:
+                break
+        el = time.perf_counter() - c0
+        t_full = el * Bn / len(done)
+        res["cpu_baseline"] = {
+            "value": 100.0 * t_roof / t_full, "unit": "% of roofline", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(done)} of {Bn} sequences, fp64 numpy, {el:.1f} s; scaled to the "
+                      "whole batch",
+            "seconds_per_step_est": t_full, "tflops": flops / t_full / 1e12,
+        }
+    print(json.dumps(res), flush=True)
+
+
 def kernel_hash():
     h = hashlib.sha256()
     for f in ("mla_main_bf16.hip", "mla_internal.h", "mla_oacc_asm.h"):
@@ -114,11 +230,15 @@ def main():
               "(the decode runs on a single GPU, with no inter-GPU sharding).", file=sys.stderr)
         sys.exit(2)
 
+    from mla_decode_attention_flashmla_amd import inputs as I
+    if args.workload in I.SPARSE_WORKLOADS:
+        run_sparse(args)
+        return
+
     import numpy as np
     import torch
 
     from mla_decode_attention_flashmla_amd import binding as B
-    from mla_decode_attention_flashmla_amd import inputs as I
 
     w = I.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
