@@ -230,7 +230,7 @@ def test_scheduler_partition_invariants():
     d = I.make_workload(w)
     d["seqlens"][5] = 2
     t = to_device(d)
-    for nwg, minb in ((256, 0), (256, 1), (13, 3), (1000, 1)):
+    for nwg, minb in ((256, 0), (256, 1), (13, 3), (1000, 1), (1000, 0), (7, 0)):
         announce(f"scheduler nwg={nwg} min_split={minb}")
         plan = B.alloc_plan(37, 2, 128, True, t["table"].shape[1], nwg)
         B.get_split_metadata(t["lens"], plan, minb)
@@ -240,19 +240,31 @@ def test_scheduler_partition_invariants():
         wg = m[32:32 + 8 * nwg].reshape(nwg, 8)
         seg = m[32 + 8 * nwg:32 + 8 * nwg + 8 * nseg].reshape(nseg, 8)
         assert nseg == 37 * 2 and m[6] == 0
+        T, n = int(m[9]), int(m[10])
+        if minb == 0:
+            # default: the fewest items whose largest is as short as with one per slot
+            c = -(-T // nwg)
+            assert n == -(-T // c), (T, nwg, n)
+        else:
+            assert n == min(max(T // minb, 1), nwg, T)
         lens = d["seqlens"]
         assert np.array_equal(seg[:, 0], np.repeat((lens + 63) // 64, 2))
         cover = [np.zeros(n, int) for n in seg[:, 0]]
         parts = np.zeros(nseg, int)
+        longest = 0
         for r in wg:
             if r[0] < 0:
                 continue
+            size = 0
             for s in range(r[0], r[2] + 1):
                 b0 = r[1] if s == r[0] else 0
                 b1 = r[3] if s == r[2] else seg[s, 0]
                 if b1 > b0:
                     cover[s][b0:b1] += 1
                     parts[s] += 1
+                    size += b1 - b0
+            longest = max(longest, size)
+        assert longest == -(-T // n)
         assert all((c == 1).all() for c in cover)
         assert np.array_equal(parts, seg[:, 3])
         multi = seg[:, 3] > 1
