@@ -110,6 +110,8 @@ int decode(int stages, int dtype, const void* q, const void* kv_cache, int64_t n
   const size_t slots = num_slots(batch, s_q, num_heads, num_workgroups);
   p.part_o = (float*)workspace;
   p.part_lse = p.part_o + slots * kGroupRows * kDv;
+  p.part_half = dtype == MLA_DTYPE_BF16;
+  p.part_scale = p.part_half ? part_scale_ptr(p.part_o, slots) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   if (stages & kStageMain) {
@@ -218,6 +220,8 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
   const size_t slots = num_slots(batch, 1, num_heads, num_workgroups);
   p.part_o = (float*)workspace;
   p.part_lse = p.part_o + slots * kGroupRows * kDv;
+  p.part_half = true;
+  p.part_scale = part_scale_ptr(p.part_o, slots);
   if (launch_main_bf16(p, st) != hipSuccess) return MLA_ERR_HIP;
   if (launch_combine(p, st) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;

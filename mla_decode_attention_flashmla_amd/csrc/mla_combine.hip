@@ -20,10 +20,13 @@ constexpr int kRowsPerBlock = 4;  // 64 threads per row, 8 columns per thread
 constexpr int kMaxSplitsLds = 1024;
 constexpr int kBatch = 4;         // parts whose O loads are in flight together
 
+// kHalf: the partial O values are fp16 under a power-of-two scale per (part, row),
+// folded here into the part's weight; otherwise fp32.
+template <bool kHalf>
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     int batch, int s_q, int heads, int nwg, float* __restrict__ out, float* __restrict__ lse_out,
     const int32_t* __restrict__ meta, const float* __restrict__ part_o,
-    const float* __restrict__ part_lse) {
+    const float* __restrict__ part_lse, const float* __restrict__ part_scale) {
   __shared__ float w_s[kRowsPerBlock][kMaxSplitsLds];
   __shared__ float lse_s[kRowsPerBlock];
   const int seg = blockIdx.x;
@@ -60,20 +63,29 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   const size_t slot0 = (size_t)sr[S_SLOT];
   // the parts must lie inside the workspace sized for this call (nwg + segments slots)
   if (sr[S_SLOT] < 0 || slot0 + (size_t)nsplit > (size_t)nwg + (size_t)gridDim.x) return;
-  const float* prow = part_o + (slot0 * kGroupRows + row_in_group) * kDv + 8 * lane;
-  const size_t pstride = (size_t)kGroupRows * kDv;  // floats from one part's row to the next's
-
+  // this thread's 8 columns of part j's row: 32 bytes of fp32 or 16 bytes of fp16
+  const size_t pstride = (size_t)kGroupRows * kDv;  // elements from one part's row to the next's
+  const size_t pbase = (slot0 * kGroupRows + row_in_group) * kDv + 8 * lane;
+  float4 pa[kBatch], pc[kBatch];
+  auto load_part = [&](int jslot, int i) {
+    if constexpr (kHalf) {
+      const uint4 raw = *(const uint4*)((const _Float16*)part_o + pbase + i * pstride);
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      const f16x2 a = __builtin_bit_cast(f16x2, raw.x), b2 = __builtin_bit_cast(f16x2, raw.y);
+      const f16x2 c = __builtin_bit_cast(f16x2, raw.z), d = __builtin_bit_cast(f16x2, raw.w);
+      pa[jslot] = make_float4((float)a[0], (float)a[1], (float)b2[0], (float)b2[1]);
+      pc[jslot] = make_float4((float)c[0], (float)c[1], (float)d[0], (float)d[1]);
+    } else {
+      pa[jslot] = *(const float4*)(part_o + pbase + i * pstride);
+      pc[jslot] = *(const float4*)(part_o + pbase + i * pstride + 4);
+    }
+  };
   // The first kBatch parts' O values are requested before the weights are known, so
   // their latency overlaps the LSE reads (every load below is independent).
-  float4 pa[kBatch], pc[kBatch];
   if (row_ok) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (j < nsplit) {
-        pa[j] = *(const float4*)(prow + j * pstride);
-        pc[j] = *(const float4*)(prow + j * pstride + 4);
-      }
-    }
+    for (int j = 0; j < kBatch; ++j)
+      if (j < nsplit) load_part(j, j);
   }
 
   // weights exp(LSE_i - LSE) for this row, computed by its 64 threads
@@ -94,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     for (int i = lane; i < nsplit; i += 64) {
       const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
       const float w = l == -INFINITY ? 0.f : expf(l - base);
-      if (i < kMaxSplitsLds) w_s[rl][i] = w;
+      const float sc = kHalf ? part_scale[(slot0 + i) * kGroupRows + row_in_group] : 1.f;
+      if (i < kMaxSplitsLds) w_s[rl][i] = w * sc;
       sum += w;
     }
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
@@ -105,10 +118,12 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   __syncthreads();
   if (!row_ok) return;
 
+  // weight of part i's stored values: exp(LSE_i - M), times its scale for fp16 partials
   auto weight = [&](int i) {
     if (i < kMaxSplitsLds) return w_s[rl][i];
     const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
-    return l == -INFINITY ? 0.f : expf(l - base);
+    const float sc = kHalf ? part_scale[(slot0 + i) * kGroupRows + row_in_group] : 1.f;
+    return l == -INFINITY ? 0.f : expf(l - base) * sc;
   };
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto add = [&](float w, const float4& a, const float4& c) {
@@ -127,12 +142,8 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   // further parts, kBatch at a time with all their loads issued first
   for (int i0 = kBatch; i0 < nsplit; i0 += kBatch) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (i0 + j < nsplit) {
-        pa[j] = *(const float4*)(prow + (i0 + j) * pstride);
-        pc[j] = *(const float4*)(prow + (i0 + j) * pstride + 4);
-      }
-    }
+    for (int j = 0; j < kBatch; ++j)
+      if (i0 + j < nsplit) load_part(j, i0 + j);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
       if (i0 + j < nsplit) add(weight(i0 + j), pa[j], pc[j]);
@@ -150,8 +161,14 @@ hipError_t launch_combine(const Problem& p, hipStream_t stream) {
   const int nseg = p.batch * groups;
   if (nseg == 0) return hipSuccess;
   dim3 grid(nseg, kGroupRows / kRowsPerBlock);
-  hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(kThreads), 0, stream, p.batch, p.s_q, p.heads,
-                     p.num_wg, p.out, p.lse, p.meta, p.part_o, p.part_lse);
+  if (p.part_half)
+    hipLaunchKernelGGL(mla_combine_kernel<true>, grid, dim3(kThreads), 0, stream, p.batch, p.s_q,
+                       p.heads, p.num_wg, p.out, p.lse, p.meta, p.part_o, p.part_lse,
+                       p.part_scale);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<false>, grid, dim3(kThreads), 0, stream, p.batch,
+                       p.s_q, p.heads, p.num_wg, p.out, p.lse, p.meta, p.part_o, p.part_lse,
+                       p.part_scale);
   return hipGetLastError();
 }
 

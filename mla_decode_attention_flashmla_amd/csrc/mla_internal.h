@@ -44,7 +44,8 @@ inline size_t meta_words(int batch, int s_q, int heads, int num_wg) {
 inline size_t num_slots(int batch, int s_q, int heads, int num_wg) {
   return (size_t)num_wg + (size_t)batch * num_groups(s_q, heads);
 }
-// workspace: partial O [slots][128][512] fp32, then partial LSE [slots][128] fp32
+// workspace: partial O [slots][128][512] fp32 (or fp16 + per-row scales), then partial
+// LSE [slots][128] fp32
 inline size_t workspace_bytes(int batch, int s_q, int heads, int num_wg) {
   return num_slots(batch, s_q, heads, num_wg) * kGroupRows * (kDv + 1) * sizeof(float);
 }
@@ -62,9 +63,15 @@ struct Problem {
   float* lse;
   int32_t* meta;
   int num_wg;
-  float* part_o;    // [slots][128][512]
+  float* part_o;    // [slots][128][512] fp32, or fp16 (part_half) in the first half
   float* part_lse;  // [slots][128]
+  float* part_scale;  // [slots][128], fp16 partials only: each row's power-of-two scale
+  bool part_half;     // partial O stored as scaled fp16 (bf16 path) instead of fp32
 };
+// With fp16 partials the per-row scales sit in the unused second half of the O region.
+inline float* part_scale_ptr(float* part_o, size_t slots) {
+  return (float*)((char*)part_o + slots * kGroupRows * kDv * 2);
+}
 
 // Sparse decode scratch, carved from the caller's workspace after the partial results:
 // the packed rows [batch * topk][576] bf16, the pool row of each packed row, the packed

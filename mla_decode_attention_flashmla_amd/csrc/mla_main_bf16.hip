@@ -54,6 +54,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -231,8 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv, int64_t num_blocks,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seqlens,
     int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
-    float* __restrict__ lse_out, int32_t* __restrict__ meta, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    float* __restrict__ lse_out, int32_t* __restrict__ meta, _Float16* __restrict__ part_o,
+    float* __restrict__ part_lse, float* __restrict__ part_scale) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -563,32 +564,61 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         inv = 0.f;
         lse_v = -INFINITY;
       }
-      float* orow;
-      float* lrow;
       if (whole) {
         const size_t ri = ((size_t)b * s_q + t) * heads + hd;
-        orow = out + ri * kDv;
-        lrow = lse_out + ri;
-      } else {
-        const int split = seg == seg_first ? split_first : 0;
-        const size_t slot_i = (size_t)sload(segt + (size_t)seg * kSegWords + S_SLOT) + split;
-        orow = part_o + (slot_i * kGroupRows + row_in_group) * kDv;
-        lrow = part_lse + slot_i * kGroupRows + row_in_group;
-      }
+        float* orow = out + ri * kDv;
 #pragma unroll
-      for (int ct = 0; ct < kCTiles; ++ct) {
-        float v[16];
-        o_read(ct, v);
-        if (row_ok) {
+        for (int ct = 0; ct < kCTiles; ++ct) {
+          float v[16];
+          o_read(ct, v);
+          if (row_ok) {
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            f32x4 o4 = {v[4 * qd] * inv, v[4 * qd + 1] * inv, v[4 * qd + 2] * inv,
-                        v[4 * qd + 3] * inv};
-            *(f32x4*)(orow + 32 * ct + 8 * qd + 4 * h) = o4;
+            for (int qd = 0; qd < 4; ++qd) {
+              f32x4 o4 = {v[4 * qd] * inv, v[4 * qd + 1] * inv, v[4 * qd + 2] * inv,
+                          v[4 * qd + 3] * inv};
+              *(f32x4*)(orow + 32 * ct + 8 * qd + 4 * h) = o4;
+            }
           }
         }
+        if (row_ok && h == 0) lse_out[ri] = lse_v;
+      } else {
+        // One part of a split segment: O_i in fp16 under a power-of-two scale per row that
+        // puts the row's largest |O_i| in [2^14, 2^15), so every value keeps fp16's 11
+        // significant bits and none overflows; the combine multiplies the scale back.
+        // Half the bytes of fp32 partials, written here and read again by the combine.
+        const int split = seg == seg_first ? split_first : 0;
+        const size_t slot_i = (size_t)sload(segt + (size_t)seg * kSegWords + S_SLOT) + split;
+        float amax = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < kCTiles; ++ct) {
+          float v[16];
+          o_read(ct, v);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
+        }
+        amax = swap_halves_max(amax) * inv;
+        int e = __builtin_amdgcn_frexp_expf(amax);   // amax in [2^(e-1), 2^e)
+        e = e < -100 ? -100 : (e > 100 ? 100 : e);
+        const float inv_s = inv * __builtin_ldexpf(1.f, 15 - e);
+        _Float16* orow = part_o + (slot_i * kGroupRows + row_in_group) * kDv;
+#pragma unroll
+        for (int ct = 0; ct < kCTiles; ++ct) {
+          float v[16];
+          o_read(ct, v);
+          if (row_ok) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+              f16x4 o4 = {(_Float16)(v[4 * qd] * inv_s), (_Float16)(v[4 * qd + 1] * inv_s),
+                          (_Float16)(v[4 * qd + 2] * inv_s), (_Float16)(v[4 * qd + 3] * inv_s)};
+              *(f16x4*)(orow + 32 * ct + 8 * qd + 4 * h) = o4;
+            }
+          }
+        }
+        if (row_ok && h == 0) {
+          part_lse[slot_i * kGroupRows + row_in_group] = lse_v;
+          part_scale[slot_i * kGroupRows + row_in_group] = __builtin_ldexpf(1.f, e - 15);
+        }
       }
-      if (row_ok && h == 0) *lrow = lse_v;
     }
     if (bad && threadIdx.x == 0)
       atomicOr(&meta[H_STATUS], (bad_block ? MLA_STATUS_BAD_BLOCK : 0) |
@@ -609,7 +639,7 @@ hipError_t launch_main_bf16(const Problem& p, hipStream_t stream) {
   hipLaunchKernelGGL(mla_main_bf16_kernel, dim3(p.num_wg), dim3(kThreads), 0, stream,
                      (const __bf16*)p.q, (const __bf16*)p.kv, p.num_blocks, p.block_table,
                      p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal, p.scale, p.out,
-                     p.lse, p.meta, p.part_o, p.part_lse);
+                     p.lse, p.meta, (_Float16*)p.part_o, p.part_lse, p.part_scale);
   return hipGetLastError();
 }
 

@@ -126,7 +126,9 @@ def test_uniform_scores_mean_and_log_n():
     np.testing.assert_allclose(lse[0], np.log(1000.0), atol=2e-6)
     np.testing.assert_allclose(lse[1], np.log(77.0), atol=2e-6)
     ref_o, _ = oracle(d)
-    assert np.abs(out - ref_o).max() < 1e-5 * np.abs(ref_o).max() + 1e-6
+    # every weight is exactly 1, so only the split parts' fp16 storage rounds: at most half
+    # an fp16 ulp of the part's largest |O| (scaled into [2^14, 2^15)), i.e. 2^-11 of it
+    assert np.abs(out - ref_o).max() < 2.0 ** -11 * np.abs(ref_o).max() + 1e-6
 
 
 def test_causal_reduction_on_device():
