@@ -164,6 +164,82 @@ def run_sparse(args):
     print(json.dumps(res), flush=True)
 
 
+APPEND_WORKLOADS = {"kv_append_b128_s2_l16384": "spec_b128_sq2_l16384"}
+
+
+def run_append(args):
+    """The latent-cache append of a decode step: the s_q new rows of each sequence of the
+    s_q = 2 workload (128 sequences of 16K tokens, 2.4 GB pool) written into its pages by
+    one mla_kv_append call.  Algorithmic bytes: the new rows read and written once, their
+    block numbers and the lengths."""
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_flashmla_amd import binding as B
+    from mla_decode_attention_flashmla_amd import inputs as I
+
+    w = I.WORKLOADS[APPEND_WORKLOADS[args.workload]]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = I.make_workload(w)
+    dev = torch.device("cuda", 0)
+    kv = torch.from_numpy(d["kv_cache"].view(np.int16)).view(torch.bfloat16).to(dev)
+    table = torch.from_numpy(d["block_table"]).to(dev)
+    lens = torch.from_numpy(d["seqlens"]).to(dev)
+    new = (torch.randn((w.batch, w.s_q, 576), generator=torch.Generator().manual_seed(w.seed))
+           * 0.5).to(torch.bfloat16).to(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        B.kv_append(new, kv, table, lens, status)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise SystemExit("device status flagged an error")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        B.kv_append(new, kv, table, lens, status)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    rows = w.batch * w.s_q
+    byt = 2 * rows * 576 * 2 + rows * 4 + w.batch * 4
+    step_s = ms_step * 1e-3
+    roof = {"bound": "hbm", "achieved": byt / step_s / 1e9, "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "mla_append_kernel"
+    roof["kernel_us"] = ms_step * 1e3
+    res = {
+        "metric": "latent-cache append GB/s as % of HBM roofline", "value": 100.0 * roof["frac"],
+        "unit": "% of roofline", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "s_new": w.s_q,
+                   "seq_len": w.context, "block_size": 64, "head_dim": 576,
+                   "parallelism": "single-gpu"},
+        "alg_bytes": byt, "roofline_us": byt / HBM_PEAK * 1e6, "wall_s": wall, "roofline": roof,
+        "note": "a few hundred KB per call: the call is launch-latency bound, not HBM bound",
+    }
+    if not args.no_cpu_baseline:
+        from oracle import mla_oracle as O
+        newb = new.view(torch.int16).cpu().numpy().view(np.uint16)
+        c0 = time.perf_counter()
+        O.kv_append(d["kv_cache"], d["block_table"], d["seqlens"], newb)
+        el = time.perf_counter() - c0
+        res["cpu_baseline"] = {
+            "value": 100.0 * (byt / el / 1e9) / (HBM_PEAK / 1e9), "unit": "% of roofline",
+            "cores": 1, "kind": "oracle",
+            "sample": f"the whole call once (the oracle copies the 2.4 GB pool, then writes "
+                      f"the rows), {el:.2f} s",
+            "seconds_per_step_est": el,
+        }
+    print(json.dumps(res), flush=True)
+
+
 def kernel_hash():
     h = hashlib.sha256()
     for f in ("mla_main_bf16.hip", "mla_internal.h", "mla_oacc_asm.h"):
@@ -233,6 +309,9 @@ def main():
     from mla_decode_attention_flashmla_amd import inputs as I
     if args.workload in I.SPARSE_WORKLOADS:
         run_sparse(args)
+        return
+    if args.workload in APPEND_WORKLOADS:
+        run_append(args)
         return
 
     import numpy as np

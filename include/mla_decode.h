@@ -185,6 +185,30 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Latent-cache append, the step before decode attention (the pages describe only the
+ * attention; this call writes the rows it reads, under the same cache layout and the
+ * same length convention).  Row t of sequence b (0 <= t < s_new) is written to
+ * logical position p = seqlens[b] - s_new + t (seqlens already count the new tokens,
+ * as mla_decode_fwd's causal mask reads them), i.e. to
+ *   kv_cache[block_table[b][p / 64]][p % 64][0:576].
+ * dtype:     MLA_DTYPE_BF16 or MLA_DTYPE_F32, the element type of new_kv and kv_cache.
+ * new_kv:    device [batch][s_new][576], contiguous, 16-byte aligned; only read.
+ * kv_cache:  device [num_blocks][64][576], 16-byte aligned; the addressed rows are
+ *            overwritten, nothing else is touched.
+ * block_table [batch][max_blocks_per_seq] int32 and seqlens [batch] int32: device; read.
+ * status:    device int32 or NULL.  A row whose position is outside
+ *            [0, 64 * max_blocks_per_seq) is skipped and MLA_STATUS_BAD_SEQLEN is OR'ed
+ *            in; a row whose block number is outside [0, num_blocks) is skipped with
+ *            MLA_STATUS_BAD_BLOCK.  The word is never cleared by the library.
+ * Asynchronous on `stream`; allocates nothing.  Rows of different calls, or two rows
+ * of one call with the same position, must not overlap in flight: the later write wins
+ * only in stream order.  Host-side errors as for mla_decode_fwd.
+ */
+int mla_kv_append(int dtype, const void* new_kv, void* kv_cache, int64_t num_blocks,
+                  const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens,
+                  int batch, int s_new, int32_t* status, void* stream);
+
+/*
  * Synchronizes `stream`, then copies the plan's device status word
  * (MLA_STATUS_* bits, 0 = clean) into *status (host pointer).
  */

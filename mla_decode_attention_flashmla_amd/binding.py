@@ -32,7 +32,7 @@ D_V = 512
 
 EXPORTS = ("mla_device_workgroups", "mla_plan_size", "mla_get_split_metadata",
            "mla_decode_fwd", "mla_decode_main", "mla_decode_combine", "mla_sparse_plan_size",
-           "mla_decode_sparse_fwd", "mla_read_status", "mla_status_string")
+           "mla_decode_sparse_fwd", "mla_kv_append", "mla_read_status", "mla_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
                                          ctypes.POINTER(c_sz)]
     lib.mla_decode_sparse_fwd.argtypes = [c_p, c_p, c_i64, c_p, c_int, c_p, c_p, c_int, c_int,
                                           c_int, c_f, c_p, c_p, c_p, c_sz, c_int, c_p, c_sz, c_p]
+    lib.mla_kv_append.argtypes = [c_int, c_p, c_p, c_i64, c_p, c_int, c_p, c_int, c_int, c_p,
+                                  c_p]
     lib.mla_read_status.argtypes = [c_p, c_p, ctypes.POINTER(ctypes.c_int32)]
     lib.mla_status_string.argtypes = [c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -225,6 +227,25 @@ def decode_sparse_fwd(q, kv_cache, block_table, seqlens, indices, scale, out, ls
         block_table.shape[1], seqlens.data_ptr(), indices.data_ptr(), topk, B, H, float(scale),
         out.data_ptr(), lse.data_ptr(), plan.meta.data_ptr(), plan.meta.numel() * 4,
         plan.num_workgroups, plan.workspace.data_ptr(), plan.workspace.numel(), _stream(stream)))
+
+
+def kv_append(new_kv, kv_cache, block_table, seqlens, status=None, stream=None) -> None:
+    """mla_kv_append: writes new_kv [B, s_new, 576] into the pages of kv_cache [n, 64, 576]
+    at positions seqlens[b] - s_new + t (seqlens count the new tokens).  status: an
+    optional device int32 tensor of one element that collects MLA_STATUS_* bits."""
+    lib = load()
+    for name, t in (("new_kv", new_kv), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seqlens", seqlens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, s_new, D = new_kv.shape
+    if (D != D_QK or kv_cache.shape[1:] != (PAGE, D_QK) or block_table.shape[0] != B
+            or seqlens.shape[0] != B or kv_cache.dtype != new_kv.dtype):
+        raise ValueError("shape/dtype mismatch with new_kv [B,s_new,576], kv [n,64,576]")
+    _check("mla_kv_append", lib.mla_kv_append(
+        _dtype_code(new_kv), new_kv.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
+        block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), B, s_new,
+        status.data_ptr() if status is not None else None, _stream(stream)))
 
 
 def read_status(plan: Plan, stream=None) -> int:

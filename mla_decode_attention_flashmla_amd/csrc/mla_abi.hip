@@ -25,6 +25,14 @@ int check_sizes(int batch, int s_q, int heads, int num_wg) {
 
 }  // namespace
 
+namespace mla {
+// mla_append.hip
+hipError_t launch_append(const void* new_kv, void* kv_cache, int64_t num_blocks,
+                         const int32_t* block_table, int max_blocks, const int32_t* seqlens,
+                         int batch, int s_new, int elem_bytes, int32_t* status,
+                         hipStream_t stream);
+}  // namespace mla
+
 extern "C" {
 
 int mla_device_workgroups(int device, int* num_workgroups) {
@@ -224,6 +232,25 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
   p.part_scale = part_scale_ptr(p.part_o, slots);
   if (launch_main_bf16(p, st) != hipSuccess) return MLA_ERR_HIP;
   if (launch_combine(p, st) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_kv_append(int dtype, const void* new_kv, void* kv_cache, int64_t num_blocks,
+                  const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens,
+                  int batch, int s_new, int32_t* status, void* stream) {
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || s_new < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return MLA_ERR_INVALID_ARG;
+  if ((int64_t)batch * s_new == 0) return MLA_OK;
+  if ((int64_t)batch * s_new > ((int64_t)1 << 31) - 64) return MLA_ERR_UNSUPPORTED;
+  if (!new_kv || !seqlens || (max_blocks_per_seq > 0 && !block_table)) return MLA_ERR_INVALID_ARG;
+  if (num_blocks > 0 && !kv_cache) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(new_kv) || (kv_cache && !aligned16(kv_cache))) return MLA_ERR_INVALID_ARG;
+  if (status && ((uintptr_t)status & 3u)) return MLA_ERR_INVALID_ARG;
+  if (launch_append(new_kv, kv_cache, num_blocks, block_table, max_blocks_per_seq, seqlens,
+                    batch, s_new, dtype == MLA_DTYPE_BF16 ? 2 : 4, status,
+                    (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
   return MLA_OK;
 }
 

@@ -25,6 +25,8 @@ A query with no visible key (n = 0) gets O = 0 and LSE = -inf.
 
 ``merge_partials`` is the log-sum-exp merge of attention results over
 disjoint key sets; it is exercised against the unsplit definition.
+``kv_append`` writes a decode step's new latent rows into the pages, where
+``gather_rows`` (and so the attention) reads them.
 """
 
 from __future__ import annotations
@@ -166,6 +168,37 @@ def mla_decode_sparse(q, kv_cache, block_table, seqlens, indices, scale, dtype="
         for t in range(s_q):
             out[b, t], lse[b, t] = attend_one(qb[t], keys, scale)
     return out, lse
+
+
+def kv_append(kv_cache, block_table, seqlens, new_kv):
+    """The cache after appending each sequence's new latent rows, and the skipped rows.
+
+    The step before decode attention writes the rows that the attention reads:
+    row t of ``new_kv[b]`` (0 <= t < s_new) becomes logical row p = L_b - s_new + t
+    of sequence b, the lengths already counting the new tokens (the convention under
+    which the causal decode gives query token t the keys up to position p).  Logical
+    row p lives at ``kv_cache[block_table[b, p // 64], p % 64]``, as in ``gather_rows``.
+    A row whose position is outside [0, 64 * table width) or whose block number is
+    outside the pool is not written; it is reported as (b, t, "seqlen" or "block").
+    Returns (a new cache array, the list of skipped rows).  Exact: values are copied.
+    """
+    out = np.array(kv_cache, copy=True)
+    new_kv = np.asarray(new_kv)
+    B, s_new = new_kv.shape[:2]
+    cap = block_table.shape[1] * PAGE
+    skipped = []
+    for b in range(B):
+        for t in range(s_new):
+            p = int(seqlens[b]) - s_new + t
+            if p < 0 or p >= cap:
+                skipped.append((b, t, "seqlen"))
+                continue
+            blk = int(block_table[b, p // PAGE])
+            if blk < 0 or blk >= out.shape[0]:
+                skipped.append((b, t, "block"))
+                continue
+            out[blk, p % PAGE] = new_kv[b, t]
+    return out, skipped
 
 
 def softmax_weights(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:

@@ -365,3 +365,66 @@ def test_sparse_nothing_selected_and_brute_force():
     bo, bl = O.brute_force([qs], [rows], float(d["scale"]), False, 1)
     np.testing.assert_allclose(o[2, 0, :2], np.array(bo[0][0]), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(l[2, 0, :2], np.array(bl[0][0]), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- latent-cache append
+
+
+def test_append_worked_placement():
+    """A hand-worked case: table [[3, 1]], length 66 after appending 3 rows, so the
+    new rows are positions 63, 64, 65 = block 3 row 63, block 1 rows 0 and 1."""
+    kv = np.arange(5 * 64 * 576, dtype=np.float64).reshape(5, 64, 576)
+    table = np.array([[3, 1]], np.int32)
+    new = -1.0 - np.arange(3 * 576, dtype=np.float64).reshape(1, 3, 576)
+    out, skipped = O.kv_append(kv, table, np.array([66], np.int32), new)
+    assert skipped == []
+    assert np.array_equal(out[3, 63], new[0, 0])
+    assert np.array_equal(out[1, 0], new[0, 1])
+    assert np.array_equal(out[1, 1], new[0, 2])
+    written = np.zeros((5, 64), bool)
+    written[3, 63] = written[1, 0] = written[1, 1] = True
+    assert np.array_equal(out[~written], kv[~written])       # nothing else moved
+    assert np.array_equal(kv[3, 63], np.arange(576) + (3 * 64 + 63) * 576.0)  # input kept
+
+
+@pytest.mark.parametrize("s_new", [1, 2])
+def test_append_then_causal_decode_equals_dense_attention(s_new):
+    """Appending the step's rows and then running causal decode with s_q = s_new equals
+    plain attention over the dense concatenation [old rows; new rows], computed with
+    pure-Python loops and no paging: query token t sees the old rows and new rows 0..t."""
+    rng = np.random.default_rng(11 + s_new)
+    old = [5, 63, 64]
+    B, H = len(old), 2
+    lens = np.array([L + s_new for L in old], np.int32)
+    nblk = (lens + 63) // 64
+    perm = rng.permutation(int(nblk.sum())).astype(np.int32)
+    table = np.full((B, int(nblk.max())), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    kv = rng.standard_normal((int(nblk.sum()), 64, 576)) * 0.5
+    old_rows = [[kv[table[b, j // 64], j % 64].tolist() for j in range(old[b])] for b in range(B)]
+    new = rng.standard_normal((B, s_new, 576)) * 0.5
+    q = rng.standard_normal((B, s_new, H, 576)) * 0.5
+    kv2, skipped = O.kv_append(kv, table, lens, new)
+    assert skipped == []
+    o, l = O.mla_decode(q, kv2, table, lens, 0.07, causal=True, dtype="f64")
+    dense = [old_rows[b] + new[b].tolist() for b in range(B)]
+    qs = [[[q[b, t, h].tolist() for h in range(H)] for t in range(s_new)] for b in range(B)]
+    bo, bl = O.brute_force(qs, dense, 0.07, True, s_new)
+    np.testing.assert_allclose(o, np.array(bo), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l, np.array(bl), rtol=1e-12)
+
+
+def test_append_skips_rows_it_cannot_place():
+    kv = np.zeros((4, 64, 576))
+    table = np.array([[0, 1], [2, -1], [3, 7]], np.int32)
+    new = np.ones((3, 2, 576))
+    # seq 0: length 1 < s_new, row 0 would be position -1; seq 1: positions 64, 65 fall in
+    # table entry -1; seq 2: position 128 is past the table, 127 is in block 7 (outside)
+    out, skipped = O.kv_append(kv, table, np.array([1, 66, 129], np.int32), new)
+    assert skipped == [(0, 0, "seqlen"), (1, 0, "block"), (1, 1, "block"), (2, 0, "block"),
+                       (2, 1, "seqlen")]
+    assert np.array_equal(out[0, 0], np.ones(576))           # seq 0 row 1 -> position 0
+    assert out.sum() == 576
