@@ -1,7 +1,8 @@
 """Throughput of MLA decode on one MI355X, as a fraction of the HBM/MFMA roofline.
 
 One step = the whole hot path on one batch: split metadata (scheduler kernel),
-main kernel, log-sum-exp combine, on inputs already resident in HBM.  Prints one
+main kernel, log-sum-exp combine, on inputs already resident in HBM, launched from
+the host (--graph: the step captured once in a HIP graph and replayed).  Prints one
 JSON line.  The default workload is the 64 x 8K-context, 128-head bf16 paged
 decode; --workload selects another seeded one.
 
@@ -297,6 +298,10 @@ def main():
     ap.add_argument("--min-split-blocks", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step captured in a HIP graph instead of launching its "
+                         "three kernels from the host (measured slower on MI355X: one graph "
+                         "launch per step costs more than the three launch gaps it removes)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy this many MiB once (counter calibration runs)")
     args = ap.parse_args()
@@ -352,12 +357,33 @@ def main():
         raise SystemExit("device status flagged an error")
 
     torch.cuda.synchronize()
+    run_step = step
+    if args.graph:
+        # the whole step (scheduler, main kernel, combine) captured once and replayed:
+        # the same three kernels with the launch gaps of a graph instead of three host
+        # launches (nothing in the step sets or copies memory)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        for _ in range(max(1, args.warmup // 10)):
+            run_step()
+        torch.cuda.synchronize()
+        if B.read_status(plan) != 0:
+            raise SystemExit("device status flagged an error (graph replay)")
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record(stream)
     for _ in range(args.steps):
-        step()
+        run_step()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -417,7 +443,8 @@ def main():
         "config": {"workload": w.name, "batch": Bn, "s_q": s_q, "heads": H,
                    "seq_len": w.context, "ragged": w.ragged, "causal": w.causal,
                    "block_size": 64, "head_dim": 576, "v_dim": 512,
-                   "num_workgroups": nwg, "parallelism": "single-gpu"},
+                   "num_workgroups": nwg, "parallelism": "single-gpu",
+                   "launch": "hip-graph" if args.graph else "eager"},
         "tflops": flops / step_s / 1e12,
         "kv_gbs": kv_bytes / step_s / 1e9,
         "alg_bytes": byt,
