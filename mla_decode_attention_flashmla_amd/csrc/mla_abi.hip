@@ -119,6 +119,7 @@ int decode(int stages, int dtype, const void* q, const void* kv_cache, int64_t n
   p.part_o = (float*)workspace;
   p.part_lse = p.part_o + slots * kGroupRows * kDv;
   p.part_half = dtype == MLA_DTYPE_BF16;
+  p.src_row = nullptr;
   p.part_scale = p.part_half ? part_scale_ptr(p.part_o, slots) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
@@ -202,8 +203,11 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
   hipStream_t st = (hipStream_t)stream;
   const size_t dense_ws = align256(mla::workspace_bytes(batch, 1, num_heads, num_workgroups));
   const SparseScratch sc = sparse_scratch((char*)workspace + dense_ws, batch, topk);
+  // Pools addressable by 32-bit byte offsets: the main kernel gathers the selected rows
+  // straight from the pool.  Larger pools: the rows are first copied into packed blocks.
+  const bool fused = num_blocks <= kMaxGatherBlocks;
   if (launch_sparse_pack(seqlens, block_table, max_blocks_per_seq, num_blocks, indices, topk,
-                         batch, kv_cache, sc, st) != hipSuccess)
+                         batch, kv_cache, sc, !fused, st) != hipSuccess)
     return MLA_ERR_HIP;
   const int chunks = topk / kPage;
   if (launch_sched(sc.packed_len, batch, 1, num_heads, 0, chunks, num_workgroups, 0, meta,
@@ -211,7 +215,8 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
     return MLA_ERR_HIP;
   Problem p;
   p.q = q;
-  p.kv = sc.packed_kv;
+  p.kv = fused ? kv_cache : sc.packed_kv;
+  p.src_row = fused ? sc.src_row : nullptr;
   p.num_blocks = (int64_t)batch * chunks;
   p.block_table = sc.packed_table;
   p.max_blocks = chunks;

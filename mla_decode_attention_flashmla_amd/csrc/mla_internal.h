@@ -67,7 +67,12 @@ struct Problem {
   float* part_lse;  // [slots][128]
   float* part_scale;  // [slots][128], fp16 partials only: each row's power-of-two scale
   bool part_half;     // partial O stored as scaled fp16 (bf16 path) instead of fp32
+  // gathered pages (bf16 path): block_table entry id names rows src_row[64*id .. +63] of
+  // the pool `kv` instead of block id; nullptr for a paged cache
+  const int32_t* src_row;
 };
+// Gathered pages address pool rows by 32-bit byte offsets: pools up to this many blocks.
+constexpr int64_t kMaxGatherBlocks = 0xffffffffLL / (kPage * kDqk * 2);
 // With fp16 partials the per-row scales sit in the unused second half of the O region.
 inline float* part_scale_ptr(float* part_o, size_t slots) {
   return (float*)((char*)part_o + slots * kGroupRows * kDv * 2);
@@ -110,8 +115,12 @@ hipError_t launch_sched(const int32_t* seqlens, int batch, int s_q, int heads, i
 hipError_t launch_main_bf16(const Problem& p, hipStream_t stream);
 hipError_t launch_main_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_combine(const Problem& p, hipStream_t stream);
+// gather: also copy the selected rows into packed blocks (the two-pass form); without
+// it only the pool-row lists, packed lengths and packed block table are written, for
+// the main kernel's gathered pages
 hipError_t launch_sparse_pack(const int32_t* seqlens, const int32_t* block_table, int max_blocks,
                               int64_t num_blocks, const int32_t* indices, int topk, int batch,
-                              const void* kv, const SparseScratch& s, hipStream_t stream);
+                              const void* kv, const SparseScratch& s, bool gather,
+                              hipStream_t stream);
 
 }  // namespace mla

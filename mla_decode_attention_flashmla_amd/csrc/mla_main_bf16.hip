@@ -192,9 +192,10 @@ __device__ __forceinline__ int sload(const int32_t* p) {
 }
 
 struct PageSrc {
-  const char* base;   // block start in global memory
-  int valid_rows;     // rows [0, valid_rows) are real keys; later rows re-read the last one
-  int load;           // 0: bad block number, nothing is read
+  const char* base;     // block start in global memory (gathered pages: the pool's start)
+  const int32_t* rows;  // gathered pages: the pool row of each of the page's 64 rows
+  int valid_rows;       // rows [0, valid_rows) are real keys; later rows re-read the last one
+  int load;             // 0: bad block number, nothing is read
 };
 
 // One of this wave's 18 loads of a page (72 per page in all) into the LDS buffer at
@@ -202,34 +203,63 @@ struct PageSrc {
 // compile-time constant), i = 16, 17 copy the tail chunks of rows 16*wave + 8*(i-16)
 // .. +7.  Rows at or past valid_rows re-read the last valid row.  Spreading the 18
 // loads over the score loop keeps the copy's LDS writes from arriving in one burst.
+//
+// Gathered pages (kGather): row r of the page is pool row src.rows[r], a row of its own
+// anywhere in the pool.  g.ridx holds this wave's 16 of them (rows 16*wave ..), read as
+// scalars when the page's source is known, and g.tail[t] each lane's row of tail load t.
+// Every entry is a real pool row (the packing pass pads a sequence's last block with its
+// last row), so no clamp is needed.  The tail loads address each lane's row by a 32-bit
+// byte offset from the pool's start, which the host guarantees by the pool's size.
+struct GatherRows {
+  int ridx[16];
+  int tail[2];
+};
+
+template <bool kGather>
 __device__ __forceinline__ void issue_page_part(int i, const PageSrc& src, uint32_t lds_addr,
                                                 int wave, int lane,
-                                                const uint32_t (&tail_lane_off)[2]) {
+                                                const uint32_t (&tail_lane_off)[2],
+                                                const GatherRows& g) {
   if (!src.load) return;
   const int vmax = src.valid_rows - 1;
   const int r0 = 16 * wave;
   const uint32_t lw = lds_addr + (uint32_t)main_row(r0);
   if (i < 16) {
-    const int rs = r0 + i < vmax ? r0 + i : vmax;
-    dma16(src.base + rs * (kDqk * 2), (uint32_t)lane * 16u, lw + main_row(i));
+    if constexpr (kGather) {
+      dma16(src.base + (size_t)(uint32_t)g.ridx[i] * (kDqk * 2), (uint32_t)lane * 16u,
+            lw + main_row(i));
+    } else {
+      const int rs = r0 + i < vmax ? r0 + i : vmax;
+      dma16(src.base + rs * (kDqk * 2), (uint32_t)lane * 16u, lw + main_row(i));
+    }
   } else {
     const int t = i - 16;
-    int row = r0 + 8 * t + (lane >> 3);
-    row = row < vmax ? row : vmax;
-    dma16(src.base, (uint32_t)row * (kDqk * 2) + tail_lane_off[t],
-          lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
+    if constexpr (kGather) {
+      dma16(src.base, (uint32_t)g.tail[t] * (uint32_t)(kDqk * 2) + tail_lane_off[t],
+            lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
+    } else {
+      int row = r0 + 8 * t + (lane >> 3);
+      row = row < vmax ? row : vmax;
+      dma16(src.base, (uint32_t)row * (kDqk * 2) + tail_lane_off[t],
+            lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
+    }
   }
 }
 constexpr int kPageParts = 18;
 
+template <bool kGather>
 __device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr, int wave,
-                                           int lane, const uint32_t (&tail_lane_off)[2]) {
+                                           int lane, const uint32_t (&tail_lane_off)[2],
+                                           const GatherRows& g) {
 #pragma unroll
-  for (int i = 0; i < kPageParts; ++i) issue_page_part(i, src, lds_addr, wave, lane, tail_lane_off);
+  for (int i = 0; i < kPageParts; ++i)
+    issue_page_part<kGather>(i, src, lds_addr, wave, lane, tail_lane_off, g);
 }
 
+template <bool kGather>
 __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kv, int64_t num_blocks,
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
+    const int32_t* __restrict__ src_row, int64_t num_blocks,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seqlens,
     int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ meta, _Float16* __restrict__ part_o,
@@ -305,10 +335,38 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   auto page_src_id = [&](int rows, int id) -> PageSrc {
     PageSrc ps;
     ps.load = (uint32_t)id < pool_blocks ? 1 : 0;
-    ps.base = (const char*)kv + (size_t)(ps.load ? (uint32_t)id : 0u) * (kPage * kDqk * 2);
+    if constexpr (kGather) {
+      ps.base = (const char*)kv;
+      ps.rows = src_row + (size_t)(ps.load ? (uint32_t)id : 0u) * kPage;
+    } else {
+      ps.base = (const char*)kv + (size_t)(ps.load ? (uint32_t)id : 0u) * (kPage * kDqk * 2);
+      ps.rows = nullptr;
+    }
     ps.valid_rows = rows;
     return ps;
   };
+  // gathered pages: this wave's 16 pool rows of a page (scalar loads), and each lane's
+  // row of the two tail loads (lane l: row 8t + l/8 of the wave's 16), handed from the
+  // scalars to the lanes through one VGPR (lane j holds row j) and a lane permute
+  GatherRows grows;
+  auto load_ridx = [&](const PageSrc& ps) {
+    if constexpr (kGather) {
+      if (ps.load) {
+        int all = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          grows.ridx[j] = sload(ps.rows + 16 * wave + j);
+          asm("v_writelane_b32 %0, %1, %2" : "+v"(all) : "s"(grows.ridx[j]), "i"(j));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          grows.tail[t] = __builtin_amdgcn_ds_bpermute((8 * t + (lane >> 3)) * 4, all);
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < 16; ++j) grows.ridx[j] = 0;
+  grows.tail[0] = grows.tail[1] = 0;
   // valid rows of page blk of a sequence of length L, clamped to 1..64 whatever the plan says
   auto page_rows = [](int L, int blk) {
     const int rem = L - blk * kPage;
@@ -367,7 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     if (first_seg) {
       PageSrc ps = page_src(seg, L, blk);
       bad_block = bad_block || ps.load == 0;
-      issue_page(ps, lds0, wave, lane, tail_lane_off);
+      load_ridx(ps);
+      issue_page<kGather>(ps, lds0, wave, lane, tail_lane_off, grows);
       first_seg = false;
     }
     o_zero();
@@ -405,8 +464,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         }
       }
       const uint32_t next_lds = lds0 + (buf ^ 1) * kBufBytes;
+      load_ridx(nps);
       if (!wave_active) {
-        issue_page(nps, next_lds, wave, lane, tail_lane_off);
+        issue_page<kGather>(nps, next_lds, wave, lane, tail_lane_off, grows);
         buf ^= 1;
         continue;
       }
@@ -448,11 +508,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         const bool part = (s & 1) == 0 && s / 2 < kPageParts;
         if (s == 0) {
           mfma_s_first(sacc[0], a0, qf[s]);
-          if (part) issue_page_part(s / 2, nps, next_lds, wave, lane, tail_lane_off);
+          if (part) issue_page_part<kGather>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows);
           mfma_s_first(sacc[1], a1, qf[s]);
         } else if (s + 1 < kKSteps) {
           mfma_s(sacc[0], a0, qf[s]);
-          if (part) issue_page_part(s / 2, nps, next_lds, wave, lane, tail_lane_off);
+          if (part) issue_page_part<kGather>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows);
           mfma_s(sacc[1], a1, qf[s]);
         } else {
           mfma_s(sacc[0], a0, qf[s]);
@@ -636,10 +696,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
 }  // namespace
 
 hipError_t launch_main_bf16(const Problem& p, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_main_bf16_kernel, dim3(p.num_wg), dim3(kThreads), 0, stream,
-                     (const __bf16*)p.q, (const __bf16*)p.kv, p.num_blocks, p.block_table,
-                     p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal, p.scale, p.out,
-                     p.lse, p.meta, (_Float16*)p.part_o, p.part_lse, p.part_scale);
+  if (p.src_row) {
+    hipLaunchKernelGGL(mla_main_bf16_kernel<true>, dim3(p.num_wg), dim3(kThreads), 0, stream,
+                       (const __bf16*)p.q, (const __bf16*)p.kv, p.src_row, p.num_blocks,
+                       p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
+                       p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
+                       p.part_scale);
+  } else {
+    hipLaunchKernelGGL(mla_main_bf16_kernel<false>, dim3(p.num_wg), dim3(kThreads), 0, stream,
+                       (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
+                       p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
+                       p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
+                       p.part_scale);
+  }
   return hipGetLastError();
 }
 

@@ -74,6 +74,13 @@ __global__ __launch_bounds__(kThreads) void mla_sparse_index_kernel(
     ++pos;
   }
   __syncthreads();
+  // the rest of the last packed block repeats its last row, so a page read through these
+  // lists (the main kernel's gathered pages) only ever addresses real pool rows
+  if (total > 0) {
+    const int32_t last = src_row[(size_t)b * topk + total - 1];
+    const int padded = (total + kPage - 1) / kPage * kPage;
+    for (int e = total + tid; e < padded; e += kThreads) src_row[(size_t)b * topk + e] = last;
+  }
   if (tid == 0) packed_len[b] = len_ok ? total : -1;
   for (int c = tid; c < chunks; c += kThreads)
     packed_table[(size_t)b * chunks + c] = bad_chunk[c] ? -1 : b * chunks + c;
@@ -100,12 +107,13 @@ __global__ __launch_bounds__(kThreads) void mla_sparse_gather_kernel(
 
 hipError_t launch_sparse_pack(const int32_t* seqlens, const int32_t* block_table, int max_blocks,
                               int64_t num_blocks, const int32_t* indices, int topk, int batch,
-                              const void* kv, const SparseScratch& s, hipStream_t stream) {
+                              const void* kv, const SparseScratch& s, bool gather,
+                              hipStream_t stream) {
   hipLaunchKernelGGL(mla_sparse_index_kernel, dim3(batch), dim3(kThreads), 0, stream, seqlens,
                      block_table, max_blocks, num_blocks, indices, topk, s.src_row, s.packed_len,
                      s.packed_table);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !gather) return e;
   hipLaunchKernelGGL(mla_sparse_gather_kernel, dim3(topk / kPage, batch), dim3(kThreads), 0,
                      stream, (const uint4*)kv, s.src_row, s.packed_len, topk,
                      (uint4*)s.packed_kv);

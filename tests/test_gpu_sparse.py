@@ -132,3 +132,31 @@ def test_sparse_full_size_workload():
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     ref_o, ref_l = oracle(d)
     check(out, lse, ref_o, ref_l, "bf16", what=w.name)
+
+
+def test_sparse_pool_beyond_32bit_offsets_uses_packed_rows():
+    """A pool too large for 32-bit row byte offsets (more than 58,254 blocks of 64 x 576
+    bf16) takes the two-pass form (rows copied into packed blocks first).  The drawn
+    blocks are placed above that limit in a 4.3 GB device pool whose other blocks are
+    zero, the block table shifted to match; the result must equal the oracle's on the
+    drawn pool and table."""
+    w = I.SparseWorkload("big_pool", 3, 128, 2000, 256, seed=31)
+    d = I.make_sparse_workload(w, pad=12)
+    ref_o, ref_l = oracle(d)
+    t = to_device(d)
+    nb = t["kv"].shape[0]
+    limit = 0xFFFFFFFF // (64 * 576 * 2)
+    base = limit + 1 - nb // 2            # drawn blocks straddle the limit
+    big = torch.zeros((base + nb, 64, 576), dtype=torch.bfloat16, device="cuda")
+    big[base:] = t["kv"]
+    table = torch.where(t["table"] >= 0, t["table"] + base, t["table"])
+    announce(f"sparse pool of {base + nb} blocks (limit {limit})")
+    Bn, _, H, _ = t["q"].shape
+    plan = B.alloc_sparse_plan(Bn, H, t["idx"].shape[1])
+    out = torch.full((Bn, 1, H, 512), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full((Bn, 1, H), 7.0, dtype=torch.float32, device="cuda")
+    B.decode_sparse_fwd(t["q"], big, table, t["lens"], t["idx"], float(d["scale"]), out, lse,
+                        plan)
+    assert B.read_status(plan) == 0
+    check(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "bf16", what="big pool")
+    del big
