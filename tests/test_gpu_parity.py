@@ -293,3 +293,20 @@ def test_full_size_workload(name, nsample):
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     ref_o, ref_l = oracle(d, batches=batches)
     check(out, lse, ref_o, ref_l, w.dtype, batches=batches, what=name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_rows_per_sequence(dtype):
+    """s_q * H at its limit (1024 rows = 8 row groups per sequence), causal, ragged, with
+    lengths of exactly s_q (the first query sees one key) up to several pages."""
+    heads, s_q = 128, 8
+    lens = [8, 9, 70, 1000]
+    w = I.Workload("maxrows", len(lens), s_q, heads, max(lens), dtype, 192, causal=True,
+                   ragged=True, seed=123)
+    d = I.make_workload(w, seqlens=lens)
+    announce(f"max rows {dtype} H={heads} s_q={s_q} lens={lens}")
+    ref_o, ref_l = oracle(d)
+    for nwg, minb in ((None, 0), (13, 1)):
+        out, lse, status, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
+        assert status == 0
+        check(out, lse, ref_o, ref_l, dtype, what=f"max rows nwg={nwg}")
