@@ -166,10 +166,13 @@ int mla_decode_combine(int dtype, const void* q, const void* kv_cache, int64_t n
  *   indices   [batch][topk] int32 (device), token positions within each sequence.
  * topk is a positive multiple of 64, at most 65536; num_blocks at most 2^25.
  *
- * One call enqueues, on `stream`: the packing of the selected rows (one kernel picks
- * and orders them, one copies them into workspace blocks), the split scheduler over
- * the packed lengths (it writes `meta`, so no separate mla_get_split_metadata call
- * is made), the main kernel and the combine.  meta/workspace: device buffers of at
+ * One call enqueues, on `stream`: one kernel that picks and orders the selected rows
+ * (their pool rows, packed lengths and a packed block table, in the workspace), the
+ * split scheduler over the packed lengths (it writes `meta`, so no separate
+ * mla_get_split_metadata call is made), the main kernel, which reads each selected row
+ * straight from the pool, and the combine.  A pool of more than 58254 blocks (past
+ * 32-bit byte offsets) instead has its selected rows copied into workspace blocks by
+ * one more kernel, which the main kernel then reads as a paged cache.  meta/workspace: device buffers of at
  * least the sizes mla_sparse_plan_size returns for the same batch, num_heads, topk and
  * num_workgroups.  Errors and device status bits as for mla_decode_fwd (a selected
  * position whose block number is outside the pool: MLA_STATUS_BAD_BLOCK and NaN for
