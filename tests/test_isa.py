@@ -25,22 +25,30 @@ def asm(tmp_path_factory):
     return out.read_text()
 
 
-def _kernel_body(asm):
-    start = asm.index("mla_main_bf16_kernel")
-    start = asm.index(":\n", start)
-    return asm[start:asm.index("s_endpgm", start)]
+def _kernel_bodies(asm):
+    """The code of each instantiation of the kernel (paged and gathered pages)."""
+    names = re.findall(r"^(_Z\w*mla_main_bf16_kernel\w*):", asm, re.M)
+    assert len(names) == 2, names
+    bodies = []
+    for n in names:
+        start = re.search(r"^" + re.escape(n) + r":", asm, re.M).start()
+        bodies.append(asm[start:asm.index("s_endpgm", start)])
+    return bodies
 
 
 def test_no_spills_and_full_agpr_file(asm):
-    assert re.search(r"ScratchSize: 0\b", asm)
-    assert re.search(r"NumAgprs: 256\b", asm)
-    assert re.search(r"Occupancy: 1\b", asm)
-    assert "scratch_" not in _kernel_body(asm)
+    assert len(re.findall(r"ScratchSize: 0\b", asm)) >= 2
+    assert not re.search(r"ScratchSize: [1-9]", asm)
+    assert len(re.findall(r"NumAgprs: 256\b", asm)) == 2
+    assert len(re.findall(r"Occupancy: 1\b", asm)) == 2
+    for body in _kernel_bodies(asm):
+        assert "scratch_" not in body
 
 
-def test_compiler_code_never_touches_agprs(asm):
+@pytest.mark.parametrize("which", [0, 1])
+def test_compiler_code_never_touches_agprs(asm, which):
     inside, bad = False, []
-    for ln in _kernel_body(asm).splitlines():
+    for ln in _kernel_bodies(asm)[which].splitlines():
         if ";;#ASMSTART" in ln:
             inside = True
             continue
@@ -53,17 +61,19 @@ def test_compiler_code_never_touches_agprs(asm):
     assert not bad, bad[:5]
 
 
-def test_mfma_count_and_no_packed_fp32(asm):
-    body = _kernel_body(asm)
+@pytest.mark.parametrize("which", [0, 1])
+def test_mfma_count_and_no_packed_fp32(asm, which):
+    body = _kernel_bodies(asm)[which]
     # 72 score + 64 PV MFMAs per page, emitted once
     assert len(re.findall(r"v_mfma_f32_32x32x16_bf16", body)) == 136
     assert not re.search(r"v_pk_(add|mul|fma)_f32", body)
 
 
-def test_valu_writes_are_fenced_before_pv_mfmas(asm):
+@pytest.mark.parametrize("which", [0, 1])
+def test_valu_writes_are_fenced_before_pv_mfmas(asm, which):
     """Between the scheduling fence before the first PV MFMA and that MFMA, only the
     wait-state nop and LDS/SALU work may appear (no VALU writes of P)."""
-    body = _kernel_body(asm)
+    body = _kernel_bodies(asm)[which]
     first_pv = body.index("v_mfma_f32_32x32x16_bf16 a[0:15]")
     fence = body.rindex("sched_barrier", 0, first_pv)
     seg = body[fence:first_pv]
@@ -73,10 +83,11 @@ def test_valu_writes_are_fenced_before_pv_mfmas(asm):
         assert not code.startswith("v_cvt") and not code.startswith("v_mul"), ln
 
 
-def test_dma_base_address_is_not_sign_extended(asm):
+@pytest.mark.parametrize("which", [0, 1])
+def test_dma_base_address_is_not_sign_extended(asm, which):
     """The 64-bit page base handed to global_load_lds is rebuilt from two readfirstlane
     halves; the low half must be zero-extended (a sign extension turned addresses with
     bit 31 set into 0xffffffff........)."""
-    body = _kernel_body(asm)
+    body = _kernel_bodies(asm)[which]
     assert "global_load_lds_dwordx4" in body
     assert "s_bfe_i64" not in body
