@@ -349,24 +349,37 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   // row of the two tail loads (lane l: row 8t + l/8 of the wave's 16), handed from the
   // scalars to the lanes through one VGPR (lane j holds row j) and a lane permute
   GatherRows grows;
-  auto load_ridx = [&](const PageSrc& ps) {
+  auto set_rows = [&]() __attribute__((always_inline)) {
+    int all = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      asm("v_writelane_b32 %0, %1, %2" : "+v"(all) : "s"(grows.ridx[j]), "i"(j));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      grows.tail[t] = __builtin_amdgcn_ds_bpermute((8 * t + (lane >> 3)) * 4, all);
+  };
+  // rows j0.. of this wave's 16 for page source ps
+  auto load_ridx = [&](const PageSrc& ps, int j0) __attribute__((always_inline)) {
     if constexpr (kGather) {
       if (ps.load) {
-        int all = 0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          grows.ridx[j] = sload(ps.rows + 16 * wave + j);
-          asm("v_writelane_b32 %0, %1, %2" : "+v"(all) : "s"(grows.ridx[j]), "i"(j));
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          grows.tail[t] = __builtin_amdgcn_ds_bpermute((8 * t + (lane >> 3)) * 4, all);
+        for (int j = 0; j < 16; ++j)
+          if (j >= j0) grows.ridx[j] = sload(ps.rows + 16 * wave + j);
       }
     }
   };
 #pragma unroll
   for (int j = 0; j < 16; ++j) grows.ridx[j] = 0;
   grows.tail[0] = grows.tail[1] = 0;
+  // gathered pages: the first 8 of the wave's rows of page pf_blk of the current
+  // segment, read one page early (at the start of the PV loop, once that page's block
+  // number has arrived), so the page's first copies never wait for a scalar load; the
+  // other 8 are read when the page starts and first used half-way through its scores
+  constexpr int kPfRows = 8;
+  int pf_ridx[kPfRows];
+  int pf_blk = -1;
+#pragma unroll
+  for (int j = 0; j < kPfRows; ++j) pf_ridx[j] = 0;
   // valid rows of page blk of a sequence of length L, clamped to 1..64 whatever the plan says
   auto page_rows = [](int L, int blk) {
     const int rem = L - blk * kPage;
@@ -425,7 +438,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     if (first_seg) {
       PageSrc ps = page_src(seg, L, blk);
       bad_block = bad_block || ps.load == 0;
-      load_ridx(ps);
+      if constexpr (kGather) {
+        load_ridx(ps, 0);
+        if (ps.load) set_rows();
+      }
       issue_page<kGather>(ps, lds0, wave, lane, tail_lane_off, grows);
       first_seg = false;
     }
@@ -436,6 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     asm volatile("s_nop 7" ::: "memory");
     float m_run = kNegBig, l_run = 0.f;
     pre_blk = -1;
+    pf_blk = -1;
     bool first_page = true;
 
     for (; blk < blk_end; ++blk) {
@@ -464,8 +481,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         }
       }
       const uint32_t next_lds = lds0 + (buf ^ 1) * kBufBytes;
-      load_ridx(nps);
+      if constexpr (kGather) {
+        if (nps.load && nseg == seg && nblk == pf_blk) {
+#pragma unroll
+          for (int j = 0; j < kPfRows; ++j) grows.ridx[j] = pf_ridx[j];
+          load_ridx(nps, kPfRows);
+        } else {
+          load_ridx(nps, 0);
+        }
+      }
       if (!wave_active) {
+        if constexpr (kGather) {
+          if (nps.load) set_rows();
+        }
         issue_page<kGather>(nps, next_lds, wave, lane, tail_lane_off, grows);
         buf ^= 1;
         continue;
@@ -505,7 +533,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         // MFMA: a vector-memory issue that stalls (the memory system is busy streaming
         // the cache) then overlaps that MFMA instead of delaying the LDS reads and MFMAs
         // behind it (~1,100 cycles per page less than issuing it first).
-        const bool part = (s & 1) == 0 && s / 2 < kPageParts;
+        // (gathered pages: the two tail copies follow the loop)
+        const bool part = (s & 1) == 0 && s / 2 < (kGather ? 16 : kPageParts);
         if (s == 0) {
           mfma_s_first(sacc[0], a0, qf[s]);
           if (part) issue_page_part<kGather>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows);
@@ -518,7 +547,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
           mfma_s(sacc[0], a0, qf[s]);
           mfma_s_last(sacc[1], a1, qf[s]);
         }
+
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kGather) {
+        // each lane's rows for the two tail copies, now that all 16 row numbers are in
+        if (nps.load) {
+          set_rows();
+          issue_page_part<kGather>(16, nps, next_lds, wave, lane, tail_lane_off, grows);
+          issue_page_part<kGather>(17, nps, next_lds, wave, lane, tail_lane_off, grows);
+        }
       }
       if (blk + 2 < blk_end) {
         pre_blk = blk + 2;
@@ -585,6 +623,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       };
       // P and (after a rescale or zeroing) O were just written by VALU: fence the
       // scheduler, then wait states before the first MFMA reads them
+      if constexpr (kGather) {
+        // rows of the page after next (its block number was read during the softmax)
+        if (pre_blk == blk + 2 && (uint32_t)pre_id < pool_blocks) {
+          const int32_t* r = src_row + (size_t)pre_id * kPage + 16 * wave;
+#pragma unroll
+          for (int j = 0; j < kPfRows; ++j) pf_ridx[j] = sload(r + j);
+          pf_blk = pre_blk;
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_nop 7" ::: "memory");
       constexpr int kPv = 4 * kCTiles;
