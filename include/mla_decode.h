@@ -67,8 +67,10 @@ extern "C" {
 #define MLA_DTYPE_F32 0
 #define MLA_DTYPE_BF16 1
 
-/* Largest s_q * num_heads per call. */
-#define MLA_MAX_ROWS 1024
+/* Largest s_q * num_heads per call (128 query tokens of 128 heads: chunked queries).
+ * Every 128 rows of a sequence form one row group that reads the sequence's whole
+ * cache, so the cache is read once per row group. */
+#define MLA_MAX_ROWS 16384
 
 /* Device status bits (mla_read_status). */
 #define MLA_STATUS_BAD_SEQLEN 1     /* L_b < 0, L_b > 64 * max_blocks_per_seq, or causal L_b < s_q */

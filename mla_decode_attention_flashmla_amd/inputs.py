@@ -71,6 +71,10 @@ WORKLOADS = {
     "long_b4_l131072": Workload("long_b4_l131072", 4, 1, 128, 131072, "bf16", 192,
                                 peak_rows=4, seed=4),
     "gate_b64_l8192": Workload("gate_b64_l8192", 64, 1, 128, 8192, "bf16", 192, seed=5),
+    # a chunk of 64 new query tokens per sequence over an 8K cache, causal (chunked
+    # queries: each token's 128 heads are one row group)
+    "chunk_b4_sq64_l8192": Workload("chunk_b4_sq64_l8192", 4, 64, 128, 8192, "bf16", 192,
+                                    causal=True, seed=6),
 }
 
 

@@ -50,7 +50,7 @@ def test_plan_size(lib):
     meta2, ws2 = B.plan_size(128, 2, 128, 256)   # two 128-row groups per sequence
     assert meta2 == (32 + 8 * 256 + 8 * 256) * 4
     with pytest.raises(B.MlaError) as e:
-        B.plan_size(1, 2, 1024, 256)              # 2048 rows > MLA_MAX_ROWS
+        B.plan_size(1, 2, 8193, 256)              # 16386 rows > MLA_MAX_ROWS
     assert e.value.code == B.MLA_ERR_UNSUPPORTED
     with pytest.raises(B.MlaError) as e:
         B.plan_size(1, 0, 16, 256)
@@ -82,7 +82,7 @@ def test_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _fwd(lib, scale=-0.1) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, causal=2) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, heads=0) == B.MLA_ERR_INVALID_ARG
-    assert _fwd(lib, s_q=2, heads=1000) == B.MLA_ERR_UNSUPPORTED
+    assert _fwd(lib, s_q=2, heads=10000) == B.MLA_ERR_UNSUPPORTED
     assert _fwd(lib, nwg=0) == B.MLA_ERR_INVALID_ARG
     assert _fwd(lib, nwg=70000) == B.MLA_ERR_UNSUPPORTED
     assert _fwd(lib, meta_bytes=16) == B.MLA_ERR_PLAN
@@ -145,5 +145,5 @@ def test_sparse_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _sparse(lib, nblk=(1 << 25) + 1) == B.MLA_ERR_INVALID_ARG
     assert _sparse(lib, meta_bytes=16) == B.MLA_ERR_PLAN
     assert _sparse(lib, ws_bytes=1024) == B.MLA_ERR_PLAN
-    assert _sparse(lib, heads=2048) == B.MLA_ERR_UNSUPPORTED
+    assert _sparse(lib, heads=16385) == B.MLA_ERR_UNSUPPORTED
     assert _sparse(lib, batch=0, q=None, out=None) == B.MLA_OK

@@ -310,3 +310,48 @@ def test_maximum_rows_per_sequence(dtype):
         out, lse, status, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
         assert status == 0
         check(out, lse, ref_o, ref_l, dtype, what=f"max rows nwg={nwg}")
+
+
+CHUNKED = [
+    # heads, s_q, seqlens: many row groups per sequence, each reading the whole cache;
+    # lengths from exactly s_q (the first query token sees one key) to several pages
+    (128, 16, [16, 17, 200, 1500]),     # 16 row groups, one query token each
+    (32, 64, [64, 65, 700]),            # 16 row groups of 4 query tokens x 32 heads
+    (128, 128, [128, 300]),             # the largest: 16384 rows, 128 groups
+]
+
+
+@pytest.mark.parametrize("heads,s_q,lens", CHUNKED)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunked_queries(heads, s_q, lens, dtype):
+    """A chunk of s_q new query tokens per sequence under the causal mask: token t of the
+    chunk sees the cache up to its own position."""
+    w = I.Workload("chunk", len(lens), s_q, heads, max(lens), dtype, 192, causal=True,
+                   ragged=True, seed=7 + s_q)
+    d = I.make_workload(w, seqlens=lens)
+    announce(f"chunked {dtype} H={heads} s_q={s_q} lens={lens}")
+    ref_o, ref_l = oracle(d)
+    for nwg, minb in ((None, 0), (29, 1)):
+        out, lse, status, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
+        assert status == 0
+        check(out, lse, ref_o, ref_l, dtype, what=f"chunked nwg={nwg}")
+
+
+def test_chunked_full_size_workload():
+    """64-token chunks of 4 sequences over 8K caches (the chunked bench workload), on
+    sampled query tokens of every sequence."""
+    w = I.WORKLOADS["chunk_b4_sq64_l8192"]
+    d = I.make_workload(w)
+    announce("full-size chunk_b4_sq64_l8192")
+    out, lse, st, _ = run(d)
+    assert st == 0 and np.isfinite(out).all() and np.isfinite(lse).all()
+    tok = [0, 1, 31, 63]
+    # the oracle on the sampled tokens: token t of the chunk sees keys up to L - 64 + t
+    ref_o = np.empty((w.batch, len(tok), w.heads, 512))
+    ref_l = np.empty((w.batch, len(tok), w.heads))
+    for k, t in enumerate(tok):
+        lens_t = (d["seqlens"] - (w.s_q - 1 - t)).astype(np.int32)
+        o, l = O.mla_decode(d["q"][:, t:t + 1], d["kv_cache"], d["block_table"], lens_t,
+                            d["scale"], False)
+        ref_o[:, k], ref_l[:, k] = o[:, 0], l[:, 0]
+    check(out[:, tok], lse[:, tok], ref_o, ref_l, "bf16", what="chunk full size")
