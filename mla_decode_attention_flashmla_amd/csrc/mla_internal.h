@@ -25,6 +25,7 @@ constexpr int32_t kMagic = 0x4D4C4132;
 enum Hdr {
   H_MAGIC = 0, H_BATCH, H_SQ, H_HEADS, H_CAUSAL, H_NUM_WG, H_STATUS, H_NUM_SEG,
   H_NUM_GROUPS, H_TOTAL_BLOCKS, H_NUM_ITEMS, H_NUM_SLOTS, H_MAX_BLOCKS,
+  H_ALIGNED,  // item size of a segment-aligned plan, 0 for a stream cut
 };
 // work-table row: first segment, first block in it, last segment, end block in it (exclusive),
 // split index of the first segment, and that segment's block count and length (so a

@@ -8,6 +8,15 @@
 // DeepSeek MLA example of the TileLang talk leaves to its author: how many
 // blocks, and which work each one takes).
 //
+// By default the plan is segment-aligned when that is cheap: every segment gets
+// ceil(nb / c) whole items of at most c blocks, with c the smallest item size for which
+// the items fit one per workgroup, so no workgroup's range crosses a segment boundary.
+// A range that crosses one costs its workgroup a second part (another Q load at its
+// share of the memory bandwidth, another partial written), ~kPartCostBlocks blocks of
+// work; so the aligned plan is taken when c exceeds the stream cut's ceil(T / slots) by
+// at most that much.  Otherwise, or with a caller-given min_split_blocks, the stream is
+// cut into near-equal ranges regardless of segment boundaries.
+//
 // Per-segment arrays live in LDS when they fit (up to kLdsSegs segments);
 // larger batches keep them in the metadata buffer itself.  Prefix sums are
 // thread-local runs plus one wave-shuffle scan of the 256 run totals.
@@ -19,6 +28,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLdsSegs = 4096;
+// Measured cost of one more part in a workgroup's range (Q load and partial write),
+// in 64-token blocks of work.
+constexpr int kPartCostBlocks = 4;
 
 // Exclusive prefix sum over the block of one value per thread; returns the total.
 __device__ int64_t block_scan_exclusive(int64_t v, int64_t& total, int64_t* wave_tot) {
@@ -72,7 +84,7 @@ __device__ inline int seg_of(const Arr& cum, int nseg, int64_t pos) {
 __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
     const int32_t* __restrict__ seqlens, int batch, int s_q, int heads, int causal,
     int max_blocks, int num_wg, int min_split_blocks, int32_t* __restrict__ meta) {
-  __shared__ int32_t l_nblk[kLdsSegs], l_cum[kLdsSegs];
+  __shared__ int32_t l_nblk[kLdsSegs], l_cum[kLdsSegs], l_item[kLdsSegs];
   __shared__ int64_t wave_tot[kThreads / 64];
   __shared__ int status_lds;
   const int tid = threadIdx.x;
@@ -83,6 +95,10 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
   int32_t* seg = wg + (size_t)kWgWords * num_wg;
   auto NB = [&](int s) -> int32_t& { return in_lds ? l_nblk[s] : seg[(size_t)s * kSegWords + S_NBLK]; };
   auto CUM = [&](int s) -> int32_t& { return in_lds ? l_cum[s] : seg[(size_t)s * kSegWords + S_CUM]; };
+  // first item of a segment (segment-aligned plans)
+  auto ITEM = [&](int s) -> int32_t& {
+    return in_lds ? l_item[s] : seg[(size_t)s * kSegWords + S_FIRST_ITEM];
+  };
 
   if (tid == 0) status_lds = 0;
   __syncthreads();
@@ -117,26 +133,73 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
   }
   __syncthreads();
 
-  // 3. cut the stream into n items, spread over the slots.  By default n is the fewest
-  // items whose largest one is as short as with one item per slot, n = ceil(T / c) with
-  // c = ceil(T / slots) blocks per item: the same critical path with fewer split parts
-  // (each part costs a partial result written and read back).  A caller-given
-  // min_split_blocks sets n = T / min_split_blocks instead.  Either way
-  // 1 <= n <= min(T, slots).
-  int64_t n;
-  if (min_split_blocks > 0) {
-    n = floordiv(T, min_split_blocks);
-  } else {
-    const int64_t c = floordiv(T + num_wg - 1, num_wg);
-    n = c > 0 ? floordiv(T + c - 1, c) : 1;
+  // 3. the item size of a segment-aligned plan, if one is taken (see the top of the file)
+  const int64_t c_min = T > 0 ? floordiv(T + num_wg - 1, num_wg) : 1;
+  int64_t c_al = 0;
+  if (min_split_blocks == 0 && T > 0 && T <= 0x7fffffffLL) {
+    // items of at most c blocks, one per workgroup: sum over segments of ceil(nb / c)
+    auto items_for = [&](int64_t c) {
+      int64_t v = 0;
+      for (int s = r0; s < r1; ++s) v += floordiv(NB(s) + c - 1, c);
+      int64_t tot;
+      block_scan_exclusive(v, tot, wave_tot);
+      return tot;
+    };
+    if (items_for(c_min) <= num_wg) {
+      c_al = c_min;
+    } else {
+      int64_t ne_run = 0;
+      for (int s = r0; s < r1; ++s) ne_run += NB(s) > 0 ? 1 : 0;
+      int64_t nonempty;
+      block_scan_exclusive(ne_run, nonempty, wave_tot);
+      if (nonempty < num_wg) {
+        // sum ceil(nb / c) <= T / c + nonempty, so c = ceil(T / (slots - nonempty)) fits;
+        // search [c_min, that] for the smallest size that fits
+        int64_t lo = c_min, hi = floordiv(T + (num_wg - nonempty) - 1, num_wg - nonempty);
+        if (hi > c_min + kPartCostBlocks) hi = c_min + kPartCostBlocks + 1;
+        while (lo < hi) {
+          const int64_t mid = (lo + hi) >> 1;
+          if (items_for(mid) <= num_wg) hi = mid; else lo = mid + 1;
+        }
+        if (lo <= c_min + kPartCostBlocks && items_for(lo) <= num_wg) c_al = lo;
+      }
+    }
   }
-  if (n > T) n = T;
-  if (n < 1) n = 1;
-  if (n > num_wg) n = num_wg;
+  const bool aligned = c_al > 0;
+  // parts of segment s in an aligned plan
+  auto parts_al = [&](int s) -> int { return (int)floordiv(NB(s) + c_al - 1, c_al); };
+
+  // 4. the items and their count n.  Aligned: segment s holds items [ITEM(s),
+  // ITEM(s) + parts), its blocks split near-evenly among them.  Stream cut: n near-equal
+  // ranges; by default the fewest items whose largest one is as short as with one item
+  // per slot, n = ceil(T / c_min) (each part costs a partial result written and read
+  // back); a caller-given min_split_blocks sets n = T / min_split_blocks instead.  Either
+  // way 1 <= n <= min(T, slots).
+  int64_t n;
+  if (aligned) {
+    int64_t v = 0;
+    for (int s = r0; s < r1; ++s) v += parts_al(s);
+    int64_t a0 = block_scan_exclusive(v, n, wave_tot);
+    for (int s = r0; s < r1; ++s) {
+      ITEM(s) = (int32_t)a0;
+      a0 += parts_al(s);
+    }
+    __syncthreads();
+  } else {
+    if (min_split_blocks > 0) {
+      n = floordiv(T, min_split_blocks);
+    } else {
+      n = c_min > 0 ? floordiv(T + c_min - 1, c_min) : 1;
+    }
+    if (n > T) n = T;
+    if (n < 1) n = 1;
+    if (n > num_wg) n = num_wg;
+  }
   // the plan stores block offsets in 32 bits: a longer stream gets no work and a status bit
   if (T == 0 || T > 0x7fffffffLL) n = 0;
   if (T > 0x7fffffffLL && tid == 0) atomicOr(&status_lds, MLA_STATUS_BAD_SEQLEN);
   auto cum_at = [&](int s) { return CUM(s); };
+  auto item_at = [&](int s) { return ITEM(s); };
   for (int w = tid; w < num_wg; w += kThreads) {
     int32_t* r = wg + (size_t)w * kWgWords;
     // slot w holds item k iff k*num_wg/n == w for some k
@@ -151,6 +214,21 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
       r[W_NBLK0] = r[W_SEQLEN0] = 0;
       continue;
     }
+    if (aligned) {
+      // the segment holding item k (segments without blocks share the next one's first
+      // item, so the last segment whose first item is <= k has blocks)
+      const int sb = seg_of(item_at, nseg, k);
+      const int j = k - ITEM(sb);
+      const int64_t nb = NB(sb), ps = parts_al(sb);
+      r[W_SEG_BEGIN] = sb;
+      r[W_BLK_BEGIN] = (int32_t)floordiv((int64_t)j * nb, ps);
+      r[W_SEG_END] = sb;
+      r[W_BLK_END] = (int32_t)floordiv((int64_t)(j + 1) * nb, ps);
+      r[W_FIRST_SPLIT] = j;
+      r[W_NBLK0] = (int32_t)nb;
+      r[W_SEQLEN0] = seg[(size_t)sb * kSegWords + S_SEQLEN];
+      continue;
+    }
     const int64_t begin = floordiv((int64_t)k * T, n), end = floordiv((int64_t)(k + 1) * T, n);
     const int sb = seg_of(cum_at, nseg, begin), se = seg_of(cum_at, nseg, end - 1);
     const int64_t cb = CUM(sb);
@@ -163,28 +241,33 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
     r[W_SEQLEN0] = seg[(size_t)sb * kSegWords + S_SEQLEN];
   }
 
-  // 4. parts per segment, 5. partial slots of segments computed in several parts
+  // 5. parts per segment, 6. partial slots of segments computed in several parts
+  auto parts_of = [&](int s, int& first) -> int {
+    const int nb = NB(s);
+    if (!nb || n == 0) {
+      first = -1;
+      return 0;
+    }
+    if (aligned) {
+      first = ITEM(s);
+      return parts_al(s);
+    }
+    const int64_t c = CUM(s);
+    first = item_of(c, T, n);
+    return item_of(c + nb - 1, T, n) - first + 1;
+  };
   run = 0;
   for (int s = r0; s < r1; ++s) {
-    const int nb = NB(s);
-    int ns = 0;
-    if (nb) {
-      const int64_t c = CUM(s);
-      ns = item_of(c + nb - 1, T, n) - item_of(c, T, n) + 1;
-    }
+    int first;
+    const int ns = parts_of(s, first);
     if (ns > 1) run += ns;
   }
   int64_t slots;
   acc = block_scan_exclusive(run, slots, wave_tot);
   for (int s = r0; s < r1; ++s) {
     int32_t* r = seg + (size_t)s * kSegWords;
-    const int nb = NB(s);
-    int ns = 0, first = -1;
-    if (nb) {
-      const int64_t c = CUM(s);
-      first = item_of(c, T, n);
-      ns = item_of(c + nb - 1, T, n) - first + 1;
-    }
+    int first;
+    const int ns = parts_of(s, first);
     r[S_NSPLIT] = ns;
     r[S_FIRST_ITEM] = first;
     r[S_SLOT] = (int32_t)acc;
@@ -206,6 +289,7 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
     meta[H_NUM_ITEMS] = (int32_t)n;
     meta[H_NUM_SLOTS] = (int32_t)slots;
     meta[H_MAX_BLOCKS] = max_blocks;
+    meta[H_ALIGNED] = aligned ? (int32_t)c_al : 0;
   }
 }
 

@@ -232,7 +232,8 @@ def test_scheduler_partition_invariants():
     d = I.make_workload(w)
     d["seqlens"][5] = 2
     t = to_device(d)
-    for nwg, minb in ((256, 0), (256, 1), (13, 3), (1000, 1), (1000, 0), (7, 0)):
+    for nwg, minb in ((256, 0), (256, 1), (13, 3), (1000, 1), (1000, 0), (7, 0), (60, 0),
+                      (100, 0)):
         announce(f"scheduler nwg={nwg} min_split={minb}")
         plan = B.alloc_plan(37, 2, 128, True, t["table"].shape[1], nwg)
         B.get_split_metadata(t["lens"], plan, minb)
@@ -242,15 +243,22 @@ def test_scheduler_partition_invariants():
         wg = m[32:32 + 8 * nwg].reshape(nwg, 8)
         seg = m[32 + 8 * nwg:32 + 8 * nwg + 8 * nseg].reshape(nseg, 8)
         assert nseg == 37 * 2 and m[6] == 0
-        T, n = int(m[9]), int(m[10])
-        if minb == 0:
-            # default: the fewest items whose largest is as short as with one per slot
-            c = -(-T // nwg)
-            assert n == -(-T // c), (T, nwg, n)
+        T, n, c_al = int(m[9]), int(m[10]), int(m[13])
+        lens = d["seqlens"]
+        nb = np.repeat((lens + 63) // 64, 2)
+        assert np.array_equal(seg[:, 0], nb)
+        c_min = -(-T // nwg)
+        if minb == 0 and c_al > 0:
+            # segment-aligned: the smallest item size >= c_min whose items fit one per
+            # workgroup, at most 4 blocks above c_min
+            assert c_min <= c_al <= c_min + 4
+            assert n == int((-(-nb // c_al)).sum()) <= nwg
+            assert c_al == c_min or int((-(-nb // (c_al - 1))).sum()) > nwg
+        elif minb == 0:
+            # stream cut: the fewest items whose largest is as short as with one per slot
+            assert n == -(-T // c_min), (T, nwg, n)
         else:
             assert n == min(max(T // minb, 1), nwg, T)
-        lens = d["seqlens"]
-        assert np.array_equal(seg[:, 0], np.repeat((lens + 63) // 64, 2))
         cover = [np.zeros(n, int) for n in seg[:, 0]]
         parts = np.zeros(nseg, int)
         longest = 0
@@ -266,7 +274,11 @@ def test_scheduler_partition_invariants():
                     parts[s] += 1
                     size += b1 - b0
             longest = max(longest, size)
-        assert longest == -(-T // n)
+        if minb == 0 and c_al > 0:
+            assert longest <= c_al
+            assert all(r[0] == r[2] for r in wg if r[0] >= 0)    # no range crosses segments
+        else:
+            assert longest == -(-T // n)
         assert all((c == 1).all() for c in cover)
         assert np.array_equal(parts, seg[:, 3])
         multi = seg[:, 3] > 1
