@@ -78,6 +78,56 @@ WORKLOADS = {
 }
 
 
+# Quantized latent cache: one 656-byte row per token, 512 latent values as fp8 e4m3 codes
+# (OCP 8-bit float: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities; the
+# all-ones exponent with all-ones mantissa is NaN; largest finite 448), the 64 rope values
+# as bf16, then the row's fp32 scale and 12 bytes of padding.  A latent value is
+# code_value * scale; the rope values are exact.
+FP8_ROW_BYTES = 656
+FP8_ROPE_OFF = 512
+FP8_SCALE_OFF = 640
+
+
+def float_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 code (ties to even, saturating at +-448) of finite float values."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    e = np.clip(e, -6, 8)
+    step = np.exp2(e - 3)                       # spacing of the codes at this magnitude
+    v = np.minimum(np.round(a / step) * step, 448.0)
+    sub = v < 2.0 ** -6
+    e2 = np.floor(np.log2(np.where(sub, 1.0, v)))
+    man = np.where(sub, v / 2.0 ** -9, (v / np.exp2(e2) - 1.0) * 8.0)
+    code = np.where(sub, man, (e2 + 7) * 8 + man).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << 7)
+
+
+def quantize_fp8_cache(kv_bits: np.ndarray) -> np.ndarray:
+    """The 656-byte-row fp8 cache of a bf16 cache [blocks, 64, 576] (uint16 bits): per row,
+    scale = max |latent| / 448 (1 for an all-zero row), codes of latent / scale, rope as is."""
+    x = bf16_bits_to_float32(kv_bits.reshape(-1, 576))
+    lat = x[:, :512].astype(np.float64)
+    amax = np.abs(lat).max(axis=1)
+    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    codes = float_to_e4m3(lat / scale.astype(np.float64)[:, None])
+    out = np.zeros((x.shape[0], FP8_ROW_BYTES), dtype=np.uint8)
+    out[:, :512] = codes
+    out[:, FP8_ROPE_OFF:FP8_SCALE_OFF] = np.ascontiguousarray(
+        kv_bits.reshape(-1, 576)[:, 512:]).view(np.uint8)
+    out[:, FP8_SCALE_OFF:FP8_SCALE_OFF + 4] = scale.view(np.uint8).reshape(-1, 4)
+    return out.reshape(kv_bits.shape[0], 64, FP8_ROW_BYTES)
+
+
+def make_fp8_workload(w: "Workload", seqlens: Optional[np.ndarray] = None) -> dict:
+    """A paged workload (as make_workload) whose cache is stored as fp8 rows: the bf16
+    cache drawn for ``w`` quantized by quantize_fp8_cache (kept under "kv_bf16")."""
+    d = make_workload(w, seqlens=seqlens)
+    d["kv_bf16"] = d["kv_cache"]
+    d["kv_cache"] = quantize_fp8_cache(d["kv_cache"])
+    return d
+
+
 def float32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (round to nearest, ties to even); returns uint16 bits.
 
@@ -234,6 +284,12 @@ class SparseWorkload:
     @property
     def scale(self) -> np.float32:
         return np.float32(float(self.scale_denominator) ** -0.5)
+
+
+# Gate-shaped decode over an fp8 latent cache (64 x 8K, 128 heads)
+FP8_WORKLOADS = {
+    "fp8_b64_l8192": Workload("fp8_b64_l8192", 64, 1, 128, 8192, "bf16", 192, seed=8),
+}
 
 
 SPARSE_WORKLOADS = {

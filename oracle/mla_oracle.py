@@ -26,7 +26,9 @@ A query with no visible key (n = 0) gets O = 0 and LSE = -inf.
 ``merge_partials`` is the log-sum-exp merge of attention results over
 disjoint key sets; it is exercised against the unsplit definition.
 ``kv_append`` writes a decode step's new latent rows into the pages, where
-``gather_rows`` (and so the attention) reads them.
+``gather_rows`` (and so the attention) reads them.  ``mla_decode_fp8`` is the same
+definition over a cache of 656-byte quantized rows (fp8 e4m3 latent codes times a
+per-row fp32 scale, bf16 rope), each row dequantized exactly before use.
 """
 
 from __future__ import annotations
@@ -199,6 +201,57 @@ def kv_append(kv_cache, block_table, seqlens, new_kv):
                 continue
             out[blk, p % PAGE] = new_kv[b, t]
     return out, skipped
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Float64 value of fp8 e4m3 codes (OCP 8-bit float): sign bit 7, exponent bits 6..3
+    with bias 7, mantissa bits 2..0; exponent 0 is subnormal (mantissa * 2^-9); exponent
+    15 with mantissa 7 is NaN; no infinities."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = (c & 7).astype(np.float64)
+    mag = np.where(ex == 0, man * 2.0 ** -9, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    mag = np.where((ex == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_rows(rows: np.ndarray) -> np.ndarray:
+    """Float64 [..., 576] rows of a quantized cache stored as 656-byte rows: 512 e4m3
+    latent codes times the row's fp32 scale (bytes 640..643), then the 64 bf16 rope
+    values (bytes 512..639)."""
+    r = np.ascontiguousarray(rows, dtype=np.uint8)
+    lead = r.shape[:-1]
+    r = r.reshape(-1, r.shape[-1])
+    scale = r[:, 640:644].copy().view(np.float32)[:, 0].astype(np.float64)
+    out = np.empty((r.shape[0], D_QK))
+    out[:, :D_V] = e4m3_value(r[:, :512]) * scale[:, None]
+    out[:, D_V:] = widen(r[:, 512:640].copy().view(np.uint16), "bf16")
+    return out.reshape(*lead, D_QK)
+
+
+def mla_decode_fp8(q, kv_fp8, block_table, seqlens, scale, causal=False,
+                   batches: Iterable[int] | None = None):
+    """MLA decode over a quantized latent cache [blocks, 64, 656] bytes: the same
+    definition as ``mla_decode`` with every key/value row dequantized exactly (fp64)
+    by ``fp8_rows``; q holds bf16 bit patterns."""
+    q = np.asarray(q)
+    B, s_q, H, D = q.shape
+    if D != D_QK or kv_fp8.shape[1:] != (PAGE, 656):
+        raise ValueError("expected q [B,s_q,H,576] and kv_fp8 [blocks,64,656]")
+    seqlens = np.asarray(seqlens)
+    check_lengths(seqlens, block_table, s_q, causal)
+    scale = float(scale)
+    out = np.full((B, s_q, H, D_V), np.nan)
+    lse = np.full((B, s_q, H), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(seqlens[b])
+        keys = fp8_rows(gather_rows(kv_fp8, block_table, b, L))
+        qb = widen(q[b], "bf16")
+        for t in range(s_q):
+            n = visible_keys(L, s_q, t, causal)
+            out[b, t], lse[b, t] = attend_one(qb[t], keys[:n], scale)
+    return out, lse
 
 
 def softmax_weights(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:

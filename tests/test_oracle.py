@@ -428,3 +428,71 @@ def test_append_skips_rows_it_cannot_place():
                        (2, 1, "seqlen")]
     assert np.array_equal(out[0, 0], np.ones(576))           # seq 0 row 1 -> position 0
     assert out.sum() == 576
+
+
+# ---------------------------------------------------------------- quantized (fp8) cache
+
+
+def test_e4m3_values_fixed_by_the_format():
+    """OCP e4m3: smallest subnormal 2^-9, largest subnormal 7*2^-9, smallest normal 2^-6,
+    1.0 = 0x38, largest finite 448 = 0x7E, NaN = 0x7F / 0xFF, signed zero."""
+    codes = np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x3F, 0x40, 0x7E, 0xFE], np.uint8)
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.875, 2.0, 448.0, -448.0]
+    got = O.e4m3_value(codes)
+    assert list(got) == want
+    assert np.signbit(got[1])
+    assert np.isnan(O.e4m3_value(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_e4m3_quantizer_is_nearest_code():
+    """The input generator's quantizer picks the nearest finite code (ties to the even
+    code), checked by brute force over all 254 finite codes; every code round-trips."""
+    grid_codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    grid = O.e4m3_value(grid_codes)
+    nz = grid != 0
+    assert np.array_equal(I.float_to_e4m3(grid[nz]), grid_codes[nz])
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 30.0, rng.standard_normal(2000) * 0.01,
+                        np.array([500.0, -1e4, 0.0])])
+    q = O.e4m3_value(I.float_to_e4m3(x))
+    err = np.abs(q - np.clip(x, -448, 448))
+    best = np.abs(grid[None, :] - np.clip(x, -448, 448)[:, None]).min(axis=1)
+    assert np.array_equal(err, best)
+
+
+def test_fp8_row_layout_worked_example():
+    """One 656-byte row by hand: codes 0x38 (1.0) and 0xC0 (-2.0), scale 0.25, rope bf16
+    0x3F80 (1.0) and 0xC000 (-2.0)."""
+    row = np.zeros(656, np.uint8)
+    row[0], row[511] = 0x38, 0xC0
+    rope = np.zeros(64, np.uint16)
+    rope[0], rope[63] = 0x3F80, 0xC000
+    row[512:640] = rope.view(np.uint8)
+    row[640:644] = np.array([0.25], np.float32).view(np.uint8)
+    v = O.fp8_rows(row)
+    assert v.shape == (576,)
+    assert v[0] == 0.25 and v[511] == -0.5 and v[512] == 1.0 and v[575] == -2.0
+    assert np.count_nonzero(v) == 4
+
+
+def test_fp8_decode_equals_bf16_decode_when_quantization_is_exact():
+    """Latent rows built on the e4m3 grid times a power of two (with 448 * 2^k in each row,
+    so the per-row scale max/448 is exactly 2^k) quantize without loss: decode over the
+    fp8 cache must then equal decode over the original bf16 cache."""
+    w = I.Workload("fp8pin", 3, 2, 4, 150, "bf16", 192, causal=True, ragged=True, seed=17)
+    d = I.make_workload(w, seqlens=[150, 2, 64])
+    rng = np.random.default_rng(18)
+    kv = d["kv_cache"].reshape(-1, 576).copy()
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes = rng.choice(finite, size=(kv.shape[0], 512))
+    k = rng.integers(-8, -1, size=kv.shape[0])
+    lat = O.e4m3_value(codes) * np.exp2(k)[:, None]
+    lat[:, 7] = 448.0 * np.exp2(k)
+    kv[:, :512] = I.float32_to_bf16_bits(lat.astype(np.float32))
+    kv = kv.reshape(d["kv_cache"].shape)
+    assert np.array_equal(O.widen(kv.reshape(-1, 576)[:, :512], "bf16"), lat)  # exact in bf16
+    fp8 = I.quantize_fp8_cache(kv)
+    o8, l8 = O.mla_decode_fp8(d["q"], fp8, d["block_table"], d["seqlens"], d["scale"], True)
+    ob, lb = O.mla_decode(d["q"], kv, d["block_table"], d["seqlens"], d["scale"], True)
+    np.testing.assert_allclose(o8, ob, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l8, lb, rtol=0, atol=1e-13)
