@@ -241,6 +241,104 @@ def run_append(args):
     print(json.dumps(res), flush=True)
 
 
+def run_fp8(args):
+    """Decode over an fp8 latent cache (656-byte rows: fp8 e4m3 latent codes, bf16 rope,
+    fp32 row scale): one mla_decode_fp8_fwd call (dequantize, scheduler, main kernel,
+    combine).  Algorithmic bytes: each row read once in its 656-byte form, plus Q, O,
+    LSE and the tables; flops as for bf16 decode."""
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_flashmla_amd import binding as B
+    from mla_decode_attention_flashmla_amd import inputs as I
+
+    w = I.FP8_WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    d = I.make_fp8_workload(w)
+    dev = torch.device("cuda", 0)
+    q = torch.from_numpy(d["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = torch.from_numpy(d["kv_cache"]).to(dev)
+    table = torch.from_numpy(d["block_table"]).to(dev)
+    lens = torch.from_numpy(d["seqlens"]).to(dev)
+    Bn, s_q, H = w.batch, w.s_q, w.heads
+    out = torch.empty((Bn, s_q, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((Bn, s_q, H), dtype=torch.float32, device=dev)
+    nwg = args.num_workgroups or B.device_workgroups(0)
+    plan = B.alloc_fp8_plan(Bn, s_q, H, w.causal, table.shape[1], nwg, dev)
+    scale = float(d["scale"])
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.decode_fp8_fwd(q, kv, table, lens, scale, out, lse, plan)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if B.read_status(plan) != 0:
+        raise SystemExit("device status flagged an error")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    lens64 = d["seqlens"].astype(np.int64)
+    kv_bytes = int(lens64.sum()) * I.FP8_ROW_BYTES
+    nblk = int(((lens64 + 63) // 64).sum())
+    byt = kv_bytes + Bn * s_q * H * (576 * 2 + 512 * 4 + 4) + nblk * 4 + Bn * 4
+    flops = 2 * H * (576 + 512) * int(lens64.sum()) * s_q
+    t_roof = max(byt / HBM_PEAK, flops / MFMA_PEAK["bf16"])
+    step_s = ms_step * 1e-3
+    if byt / HBM_PEAK >= flops / MFMA_PEAK["bf16"]:
+        roof = {"bound": "hbm", "achieved": byt / step_s / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / step_s / 1e12,
+                "peak": MFMA_PEAK["bf16"] / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    # the dequantize pass and the decode share the work, so the roofline covers the call
+    roof["kernel"] = "mla_decode_fp8_fwd (dequantize, scheduler, main, combine)"
+    roof["kernel_us"] = ms_step * 1e3
+    res = {
+        "metric": METRIC, "value": 100.0 * t_roof / step_s, "unit": "% of roofline",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": Bn, "s_q": s_q, "heads": H,
+                   "seq_len": w.context, "kv_format": "fp8 e4m3 + fp32 row scale, bf16 rope",
+                   "block_size": 64, "head_dim": 576, "v_dim": 512, "num_workgroups": nwg,
+                   "parallelism": "single-gpu"},
+        "tflops": flops / step_s / 1e12, "kv_gbs": kv_bytes / step_s / 1e9,
+        "alg_bytes": byt, "alg_flops": flops, "roofline_us": t_roof * 1e6, "wall_s": wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import mla_oracle as O
+        done = []
+        c0 = time.perf_counter()
+        for b in range(Bn):
+            O.mla_decode_fp8(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], scale,
+                             w.causal, batches=[b])
+            done.append(b)
+            if time.perf_counter() - c0 >= args.cpu_budget:
+                break
+        el = time.perf_counter() - c0
+        t_full = el * Bn / len(done)
+        res["cpu_baseline"] = {
+            "value": 100.0 * t_roof / t_full, "unit": "% of roofline",
+            "cores": os.cpu_count() or 1, "kind": "oracle",
+            "sample": f"{len(done)} of {Bn} sequences, fp64 numpy, {el:.1f} s; scaled to the "
+                      "whole batch",
+            "seconds_per_step_est": t_full,
+        }
+    print(json.dumps(res), flush=True)
+
+
 def kernel_hash():
     h = hashlib.sha256()
     for f in ("mla_main_bf16.hip", "mla_internal.h", "mla_oacc_asm.h"):
@@ -317,6 +415,9 @@ def main():
         return
     if args.workload in APPEND_WORKLOADS:
         run_append(args)
+        return
+    if args.workload in I.FP8_WORKLOADS:
+        run_fp8(args)
         return
 
     import numpy as np

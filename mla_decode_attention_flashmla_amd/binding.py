@@ -32,7 +32,8 @@ D_V = 512
 
 EXPORTS = ("mla_device_workgroups", "mla_plan_size", "mla_get_split_metadata",
            "mla_decode_fwd", "mla_decode_main", "mla_decode_combine", "mla_sparse_plan_size",
-           "mla_decode_sparse_fwd", "mla_kv_append", "mla_read_status", "mla_status_string")
+           "mla_decode_sparse_fwd", "mla_fp8_plan_size", "mla_decode_fp8_fwd", "mla_kv_append",
+           "mla_read_status", "mla_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -67,6 +68,10 @@ def load() -> ctypes.CDLL:
                                          ctypes.POINTER(c_sz)]
     lib.mla_decode_sparse_fwd.argtypes = [c_p, c_p, c_i64, c_p, c_int, c_p, c_p, c_int, c_int,
                                           c_int, c_f, c_p, c_p, c_p, c_sz, c_int, c_p, c_sz, c_p]
+    lib.mla_fp8_plan_size.argtypes = [c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(c_sz),
+                                      ctypes.POINTER(c_sz)]
+    lib.mla_decode_fp8_fwd.argtypes = [c_p, c_p, c_i64, c_p, c_int, c_p, c_int, c_int, c_int,
+                                       c_int, c_f, c_p, c_p, c_p, c_sz, c_int, c_p, c_sz, c_p]
     lib.mla_kv_append.argtypes = [c_int, c_p, c_p, c_i64, c_p, c_int, c_p, c_int, c_int, c_p,
                                   c_p]
     lib.mla_read_status.argtypes = [c_p, c_p, ctypes.POINTER(ctypes.c_int32)]
@@ -227,6 +232,49 @@ def decode_sparse_fwd(q, kv_cache, block_table, seqlens, indices, scale, out, ls
         block_table.shape[1], seqlens.data_ptr(), indices.data_ptr(), topk, B, H, float(scale),
         out.data_ptr(), lse.data_ptr(), plan.meta.data_ptr(), plan.meta.numel() * 4,
         plan.num_workgroups, plan.workspace.data_ptr(), plan.workspace.numel(), _stream(stream)))
+
+
+def fp8_plan_size(batch: int, s_q: int, heads: int, max_blocks: int,
+                  num_workgroups: int) -> tuple[int, int]:
+    m, w = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mla_fp8_plan_size", load().mla_fp8_plan_size(
+        batch, s_q, heads, max_blocks, num_workgroups, ctypes.byref(m), ctypes.byref(w)))
+    return m.value, w.value
+
+
+def alloc_fp8_plan(batch: int, s_q: int, heads: int, causal: bool, max_blocks: int,
+                   num_workgroups: Optional[int] = None, device=None) -> Plan:
+    """Allocate (with torch) the metadata and workspace of decode over an fp8 cache."""
+    import torch
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    if num_workgroups is None:
+        num_workgroups = device_workgroups(device.index or 0)
+    mb, wb = fp8_plan_size(batch, s_q, heads, max_blocks, num_workgroups)
+    meta = torch.empty(mb // 4, dtype=torch.int32, device=device)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=device)
+    return Plan(meta, ws, batch, s_q, heads, int(causal), max_blocks, num_workgroups)
+
+
+def decode_fp8_fwd(q, kv_fp8, block_table, seqlens, scale, out, lse, plan: Plan,
+                   stream=None) -> None:
+    """mla_decode_fp8_fwd: q bf16 [B,s_q,H,576], kv_fp8 uint8 [n,64,656] (fp8 latent codes,
+    bf16 rope, fp32 row scale) -> out [B,s_q,H,512], lse [B,s_q,H]."""
+    lib = load()
+    for name, t in (("q", q), ("kv_fp8", kv_fp8), ("block_table", block_table),
+                    ("seqlens", seqlens), ("out", out), ("lse", lse)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, s_q, H, D = q.shape
+    if (D != D_QK or tuple(kv_fp8.shape[1:]) != (PAGE, 656) or kv_fp8.element_size() != 1
+            or block_table.shape[0] != B or tuple(out.shape) != (B, s_q, H, D_V)
+            or tuple(lse.shape) != (B, s_q, H) or _dtype_code(q) != MLA_DTYPE_BF16):
+        raise ValueError("shape/dtype mismatch with bf16 q [B,s_q,H,576], kv_fp8 [n,64,656]")
+    _check("mla_decode_fp8_fwd", lib.mla_decode_fp8_fwd(
+        q.data_ptr(), kv_fp8.data_ptr(), kv_fp8.shape[0], block_table.data_ptr(),
+        block_table.shape[1], seqlens.data_ptr(), B, s_q, H, plan.causal, float(scale),
+        out.data_ptr(), lse.data_ptr(), plan.meta.data_ptr(), plan.meta.numel() * 4,
+        plan.num_workgroups, plan.workspace.data_ptr(), plan.workspace.numel(),
+        _stream(stream)))
 
 
 def kv_append(new_kv, kv_cache, block_table, seqlens, status=None, stream=None) -> None:

@@ -147,3 +147,31 @@ def test_sparse_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _sparse(lib, ws_bytes=1024) == B.MLA_ERR_PLAN
     assert _sparse(lib, heads=16385) == B.MLA_ERR_UNSUPPORTED
     assert _sparse(lib, batch=0, q=None, out=None) == B.MLA_OK
+
+
+def _fp8(lib, **kw):
+    a = dict(q=4096, kv=8192, nblk=4, table=12288, maxb=4, lens=16384, batch=1, s_q=1,
+             heads=16, causal=0, scale=0.1, out=24576, lse=28672, meta=32768,
+             meta_bytes=1 << 20, nwg=8, ws=36864, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mla_decode_fp8_fwd(a["q"], a["kv"], a["nblk"], a["table"], a["maxb"], a["lens"],
+                                  a["batch"], a["s_q"], a["heads"], a["causal"], a["scale"],
+                                  a["out"], a["lse"], a["meta"], a["meta_bytes"], a["nwg"],
+                                  a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_fp8_decode_rejects_bad_arguments_without_touching_hip(lib):
+    meta, ws = B.fp8_plan_size(2, 1, 128, 10, 256)
+    dense = B.plan_size(2, 1, 128, 256)[1]
+    # the dense workspace, then 2 x 10 bf16 blocks of 64 x 576, then the packed table
+    assert ws >= dense + 2 * 10 * 64 * 576 * 2 + 2 * 10 * 4
+    assert meta == B.plan_size(2, 1, 128, 256)[0]
+    assert _fp8(lib, scale=0.0) == B.MLA_ERR_INVALID_ARG
+    assert _fp8(lib, causal=3) == B.MLA_ERR_INVALID_ARG
+    assert _fp8(lib, q=4100) == B.MLA_ERR_INVALID_ARG
+    assert _fp8(lib, kv=8200) == B.MLA_ERR_INVALID_ARG         # rows need 16-byte alignment
+    assert _fp8(lib, maxb=-1) == B.MLA_ERR_INVALID_ARG
+    assert _fp8(lib, heads=16385) == B.MLA_ERR_UNSUPPORTED
+    assert _fp8(lib, meta_bytes=16) == B.MLA_ERR_PLAN
+    assert _fp8(lib, ws_bytes=1024) == B.MLA_ERR_PLAN
+    assert _fp8(lib, batch=0, q=None, out=None) == B.MLA_OK
