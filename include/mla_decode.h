@@ -190,10 +190,10 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * MLA decode over a quantized latent cache (first form: dequantize, then decode).  The
- * pages name dequantization and mixed-precision layouts among what a kernel compiler
- * must handle (the TileLang talk's "Why a new DSL?" and "What is TileLang?" sections);
- * the row format is this library's own:
+ * MLA decode over a quantized latent cache.  The pages name dequantization and
+ * mixed-precision layouts among what a kernel compiler must handle (the TileLang talk's
+ * "Why a new DSL?" and "What is TileLang?" sections); the row format is this library's
+ * own:
  *   kv_fp8  [num_blocks][64][656] bytes (device, 16-byte aligned), one row per token:
  *           bytes 0..511    the 512 latent values as fp8 e4m3 codes (OCP 8-bit float:
  *                           sign, 4 exponent bits with bias 7, 3 mantissa bits, no
@@ -201,13 +201,16 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
  *           bytes 512..639  the 64 rope values as bf16,
  *           bytes 640..643  the row's fp32 scale (latent value = code value * scale),
  *           bytes 644..655  padding.
+ * The scale must be a positive normal power of two (2^-126 .. 2^127), as in the OCP
+ * microscaling formats' shared scales: the hardware conversion applies only its exponent
+ * field, so any other value gives an unspecified result (it is not checked).  With such
+ * a scale every latent value is exact in bf16.
  * Everything else as mla_decode_fwd with dtype bf16 (q bf16, out/lse fp32, the same
- * definition over the dequantized rows).  One call enqueues: a kernel that writes every
- * block a sequence reads as bf16 rows (value * scale rounded to nearest even) into the
- * workspace together with a packed block table, the split scheduler (it writes `meta`),
- * the main kernel and the combine.  meta/workspace: device buffers of at least the sizes
- * mla_fp8_plan_size returns; the workspace holds batch * max_blocks_per_seq bf16 blocks
- * (73728 bytes each).  Errors and status bits as for mla_decode_fwd (a block number
+ * definition over the dequantized rows).  One call enqueues the split scheduler (it
+ * writes `meta`), the main kernel, which copies each 656-byte-row page into LDS and
+ * widens it there to bf16 before the page's products, and the combine.  meta/workspace:
+ * device buffers of at least the sizes mla_fp8_plan_size returns (the same as
+ * mla_plan_size's).  Errors and status bits as for mla_decode_fwd (a block number
  * outside the pool: MLA_STATUS_BAD_BLOCK and NaN for that sequence).
  */
 int mla_fp8_plan_size(int batch, int s_q, int num_heads, int max_blocks_per_seq,

@@ -13,8 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_decode.so")
 SOURCES = ["mla_abi.hip", "mla_sched.hip", "mla_main_bf16.hip", "mla_main_f32.hip",
-           "mla_combine.hip", "mla_sparse.hip", "mla_append.hip",
-           "mla_fp8.hip"]
+           "mla_combine.hip", "mla_sparse.hip", "mla_append.hip"]
 ARCH = "gfx950"
 
 

@@ -26,10 +26,6 @@ int check_sizes(int batch, int s_q, int heads, int num_wg) {
 }  // namespace
 
 namespace mla {
-// mla_fp8.hip
-hipError_t launch_fp8_dequant(const void* kv8, int64_t num_blocks, const int32_t* block_table,
-                              int max_blocks, const int32_t* seqlens, int batch, void* pool,
-                              int32_t* packed_table, hipStream_t stream);
 // mla_append.hip
 hipError_t launch_append(const void* new_kv, void* kv_cache, int64_t num_blocks,
                          const int32_t* block_table, int max_blocks, const int32_t* seqlens,
@@ -124,6 +120,7 @@ int decode(int stages, int dtype, const void* q, const void* kv_cache, int64_t n
   p.part_lse = p.part_o + slots * kGroupRows * kDv;
   p.part_half = dtype == MLA_DTYPE_BF16;
   p.src_row = nullptr;
+  p.fp8 = false;
   p.part_scale = p.part_half ? part_scale_ptr(p.part_o, slots) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
@@ -221,6 +218,7 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
   p.q = q;
   p.kv = fused ? kv_cache : sc.packed_kv;
   p.src_row = fused ? sc.src_row : nullptr;
+  p.fp8 = false;
   p.num_blocks = (int64_t)batch * chunks;
   p.block_table = sc.packed_table;
   p.max_blocks = chunks;
@@ -244,12 +242,6 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
   return MLA_OK;
 }
 
-// fp8 decode workspace: the dense decode's partial results, then the dequantized pool
-// [batch * max_blocks][64][576] bf16, then the packed table [batch * max_blocks] int32
-static size_t fp8_pool_bytes(int batch, int max_blocks) {
-  return align256((size_t)batch * max_blocks * kPage * kDqk * 2);
-}
-
 int mla_fp8_plan_size(int batch, int s_q, int num_heads, int max_blocks_per_seq,
                       int num_workgroups, size_t* meta_bytes, size_t* workspace_bytes) {
   if (!meta_bytes || !workspace_bytes) return MLA_ERR_INVALID_ARG;
@@ -258,9 +250,7 @@ int mla_fp8_plan_size(int batch, int s_q, int num_heads, int max_blocks_per_seq,
   if (max_blocks_per_seq < 0) return MLA_ERR_INVALID_ARG;
   if ((int64_t)batch * max_blocks_per_seq > (int64_t)1 << 25) return MLA_ERR_UNSUPPORTED;
   *meta_bytes = meta_words(batch, s_q, num_heads, num_workgroups) * sizeof(int32_t);
-  *workspace_bytes = align256(mla::workspace_bytes(batch, s_q, num_heads, num_workgroups)) +
-                     fp8_pool_bytes(batch, max_blocks_per_seq) +
-                     align256((size_t)batch * max_blocks_per_seq * 4);
+  *workspace_bytes = mla::workspace_bytes(batch, s_q, num_heads, num_workgroups);
   return MLA_OK;
 }
 
@@ -288,20 +278,14 @@ int mla_decode_fp8_fwd(const void* q, const void* kv_fp8, int64_t num_blocks,
   if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARG;
 
   hipStream_t st = (hipStream_t)stream;
-  const size_t dense_ws = align256(mla::workspace_bytes(batch, s_q, num_heads, num_workgroups));
-  char* pool = (char*)workspace + dense_ws;
-  int32_t* packed_table = (int32_t*)(pool + fp8_pool_bytes(batch, max_blocks_per_seq));
-  if (launch_fp8_dequant(kv_fp8, num_blocks, block_table, max_blocks_per_seq, seqlens, batch,
-                         pool, packed_table, st) != hipSuccess)
-    return MLA_ERR_HIP;
   if (launch_sched(seqlens, batch, s_q, num_heads, causal, max_blocks_per_seq, num_workgroups, 0,
                    meta, st) != hipSuccess)
     return MLA_ERR_HIP;
   Problem p;
   p.q = q;
-  p.kv = pool;
-  p.num_blocks = (int64_t)batch * max_blocks_per_seq;
-  p.block_table = packed_table;
+  p.kv = kv_fp8;
+  p.num_blocks = num_blocks;
+  p.block_table = block_table;
   p.max_blocks = max_blocks_per_seq;
   p.seqlens = seqlens;
   p.batch = batch;
@@ -319,6 +303,7 @@ int mla_decode_fp8_fwd(const void* q, const void* kv_fp8, int64_t num_blocks,
   p.part_half = true;
   p.part_scale = part_scale_ptr(p.part_o, slots);
   p.src_row = nullptr;
+  p.fp8 = true;
   if (launch_main_bf16(p, st) != hipSuccess) return MLA_ERR_HIP;
   if (launch_combine(p, st) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;

@@ -71,6 +71,9 @@ struct Problem {
   // gathered pages (bf16 path): block_table entry id names rows src_row[64*id .. +63] of
   // the pool `kv` instead of block id; nullptr for a paged cache
   const int32_t* src_row;
+  // fp8 pages (bf16 path): kv holds 656-byte rows (e4m3 latent codes, bf16 rope, a
+  // power-of-two fp32 scale), widened to bf16 in LDS by the main kernel
+  bool fp8;
 };
 // Gathered pages address pool rows by 32-bit byte offsets: pools up to this many blocks.
 constexpr int64_t kMaxGatherBlocks = 0xffffffffLL / (kPage * kDqk * 2);

@@ -115,6 +115,25 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// 4 bytes per lane from global into LDS at m0 + 4 * lane (the fp8 rows' scales)
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  lds_addr = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  sbase = (const void*)(uintptr_t)((hi << 32) | lo);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %3 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
 __device__ __forceinline__ float swap_halves_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -215,14 +234,46 @@ struct GatherRows {
   int tail[2];
 };
 
-template <bool kGather>
+//
+// fp8 pages (kFp8): rows of 656 bytes (512 e4m3 codes, 64 bf16 rope values, the fp32
+// power-of-two scale).  Parts 0..7 copy the codes of row pairs (2p, 2p+1), p = 8*wave +
+// i, into the main slot of row 2p (row 2p's codes, then row 2p+1's); parts 8, 9 copy the
+// rope values into the tail region as for bf16 pages; part 10 copies the wave's 16
+// scales to the scale area.  fp8_convert() then widens the codes in place to the bf16
+// main layout before the page's scores.
+constexpr int kFp8RowBytes = 656;
+constexpr int kFp8Parts = 11;
+// per-lane byte offsets of the fp8 copies of a full page, relative to the first row of
+// each part: codes (lane -> row (lane/32), 16 bytes at 16*(lane%32)), the two rope parts
+// (lane -> row lane/8, the swizzled rope chunk) and the scales (lane -> row lane%16)
+struct Fp8Lanes {
+  uint32_t codes, tail[2], scale;
+};
+
+template <bool kGather, bool kFp8>
 __device__ __forceinline__ void issue_page_part(int i, const PageSrc& src, uint32_t lds_addr,
                                                 int wave, int lane,
                                                 const uint32_t (&tail_lane_off)[2],
-                                                const GatherRows& g) {
+                                                const GatherRows& g, uint32_t scale_lds,
+                                                const Fp8Lanes& f) {
   if (!src.load) return;
   const int vmax = src.valid_rows - 1;
   const int r0 = 16 * wave;
+  if constexpr (kFp8) {
+    // fp8 pages reach here only full (a segment's partial last page goes through
+    // issue_fp8_partial): a scalar base per part, one per-lane offset per kind
+    if (i < 8) {
+      const int p = 8 * wave + i;
+      dma16(src.base + 2 * p * kFp8RowBytes, f.codes, lds_addr + main_row(2 * p));
+    } else if (i < 10) {
+      const int t = i - 8;
+      dma16(src.base + (r0 + 8 * t) * kFp8RowBytes, f.tail[t],
+            lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
+    } else if (i == 10) {
+      dma4(src.base + r0 * kFp8RowBytes, f.scale, scale_lds + wave * 256);
+    }
+    return;
+  }
   const uint32_t lw = lds_addr + (uint32_t)main_row(r0);
   if (i < 16) {
     if constexpr (kGather) {
@@ -247,16 +298,80 @@ __device__ __forceinline__ void issue_page_part(int i, const PageSrc& src, uint3
 }
 constexpr int kPageParts = 18;
 
-template <bool kGather>
-__device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr, int wave,
-                                           int lane, const uint32_t (&tail_lane_off)[2],
-                                           const GatherRows& g) {
+// fp8: all 11 parts of a partial page (a segment's last), rows at or past its length
+// re-reading the last valid row; issued at once where the page's source is known
+__device__ __forceinline__ void issue_fp8_partial(const PageSrc& src, uint32_t lds_addr,
+                                                  int wave, int lane, uint32_t scale_lds,
+                                                  const Fp8Lanes& f) {
+  if (!src.load) return;
+  const int vmax = src.valid_rows - 1;
+  const int r0 = 16 * wave;
+  // lane values computed here (not hoisted to the kernel's start and kept live)
+  asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int i = 0; i < kPageParts; ++i)
-    issue_page_part<kGather>(i, src, lds_addr, wave, lane, tail_lane_off, g);
+  for (int i = 0; i < 8; ++i) {
+    const int p = 8 * wave + i;
+    int row = 2 * p + (lane >> 5);
+    row = row < vmax ? row : vmax;
+    dma16(src.base, (uint32_t)row * kFp8RowBytes + (uint32_t)(lane & 31) * 16u,
+          lds_addr + main_row(2 * p));
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    int row = r0 + 8 * t + (lane >> 3);
+    row = row < vmax ? row : vmax;
+    dma16(src.base, (uint32_t)row * kFp8RowBytes + f.tail[t] - (uint32_t)(lane >> 3) * kFp8RowBytes,
+          lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
+  }
+  int row = r0 + (lane & 15);
+  row = row < vmax ? row : vmax;
+  dma4(src.base, (uint32_t)row * kFp8RowBytes + 640u, scale_lds + wave * 256);
 }
 
-template <bool kGather>
+template <bool kGather, bool kFp8>
+__device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr, int wave,
+                                           int lane, const uint32_t (&tail_lane_off)[2],
+                                           const GatherRows& g, uint32_t scale_lds,
+                                           const Fp8Lanes& f) {
+  if constexpr (kFp8) {
+    if (src.valid_rows < kPage) {
+      issue_fp8_partial(src, lds_addr, wave, lane, scale_lds, f);
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < (kFp8 ? kFp8Parts : kPageParts); ++i)
+    issue_page_part<kGather, kFp8>(i, src, lds_addr, wave, lane, tail_lane_off, g, scale_lds, f);
+}
+
+// fp8 pages: widen this wave's 8 row pairs from e4m3 codes to the bf16 main layout in
+// place.  One ds_read_b128 per lane reads 16 codes (lanes 0..31: row 2p, lanes 32..63:
+// row 2p+1) before any lane writes, so row 2p's bf16 may overwrite row 2p+1's codes.
+// The hardware conversion applies the row's scale, a power of two, exactly.
+__device__ __forceinline__ void fp8_convert(uint32_t page_lds, uint32_t scale_lds, int wave,
+                                            int lane) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __attribute__((address_space(3))) float lds_f32;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = 8 * wave + i;
+    const int row = 2 * p + (lane >> 5);
+    const u32x4 c = *(const lds_u32x4*)(uintptr_t)(page_lds + main_row(2 * p) + 16u * lane);
+    const float sc = *(const lds_f32*)(uintptr_t)(scale_lds + (row >> 4) * 256 + (row & 15) * 4);
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], sc, false));
+      o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], sc, true));
+    }
+    const uint32_t dst = page_lds + main_row(row) + 32u * (lane & 31);
+    *(lds_u32x4*)(uintptr_t)dst = (u32x4){o[0], o[1], o[2], o[3]};
+    *(lds_u32x4*)(uintptr_t)(dst + 16) = (u32x4){o[4], o[5], o[6], o[7]};
+  }
+}
+
+template <bool kGather, bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ src_row, int64_t num_blocks,
@@ -264,7 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ meta, _Float16* __restrict__ part_o,
     float* __restrict__ part_lse, float* __restrict__ part_scale) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+  // two page buffers; fp8 pages add 1 KiB of row scales
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + (kFp8 ? 1024 : 0)];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;     // which half of the wave (token/column sub-block)
@@ -307,6 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   const int M = s_q * heads;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  const uint32_t scale_lds = lds0 + 2 * kBufBytes;  // fp8 pages: the page's 64 row scales
   // tail loads of rows 16*wave + 8i .. +7: lane -> row 8g + lane/8 (g = 2*wave + i), LDS
   // position lane%8, which holds chunk (lane%8) ^ ((row>>1)&7) = (lane%8) ^ ((4i + lane/16) & 7)
   uint32_t tail_lane_off[2];
@@ -314,6 +431,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   for (int i = 0; i < 2; ++i)
     tail_lane_off[i] = (uint32_t)((64 + ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7))) * 16);
   const float scale_log2 = scale * kLog2e;
+  Fp8Lanes f8l;
+  if constexpr (kFp8) {
+    // the tail offset's chunk part is tail_lane_off minus the bf16 row's 1024-byte main part
+    f8l.codes = (uint32_t)(lane >> 5) * kFp8RowBytes + (uint32_t)(lane & 31) * 16u;
+    f8l.tail[0] = (uint32_t)(lane >> 3) * kFp8RowBytes + tail_lane_off[0] - 512u;
+    f8l.tail[1] = (uint32_t)(lane >> 3) * kFp8RowBytes + tail_lane_off[1] - 512u;
+    f8l.scale = (uint32_t)(lane & 15) * kFp8RowBytes + 640u;
+  } else {
+    f8l.codes = f8l.tail[0] = f8l.tail[1] = f8l.scale = 0;
+  }
 
   // per-lane LDS byte offsets of the K (row-wise) and V (transposed) reads
   //   K: row l32 (+32 per token tile), 16-byte chunk 2s + h
@@ -338,6 +465,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     if constexpr (kGather) {
       ps.base = (const char*)kv;
       ps.rows = src_row + (size_t)(ps.load ? (uint32_t)id : 0u) * kPage;
+    } else if constexpr (kFp8) {
+      ps.base = (const char*)kv + (size_t)(ps.load ? (uint32_t)id : 0u) * (kPage * kFp8RowBytes);
+      ps.rows = nullptr;
     } else {
       ps.base = (const char*)kv + (size_t)(ps.load ? (uint32_t)id : 0u) * (kPage * kDqk * 2);
       ps.rows = nullptr;
@@ -442,7 +572,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         load_ridx(ps, 0);
         if (ps.load) set_rows();
       }
-      issue_page<kGather>(ps, lds0, wave, lane, tail_lane_off, grows);
+      issue_page<kGather, kFp8>(ps, lds0, wave, lane, tail_lane_off, grows, scale_lds, f8l);
       first_seg = false;
     }
     o_zero();
@@ -467,6 +597,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       }
       wait_dma();
       __syncthreads();
+      if constexpr (kFp8) {
+        // widen the page's codes to bf16 before any wave reads it or copies the next
+        // page's scales over this one's
+        fp8_convert(lds0 + buf * kBufBytes, scale_lds, wave, lane);
+        __syncthreads();
+      }
       PageSrc nps;
       nps.load = 0;
       if (has_next) {
@@ -481,6 +617,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         }
       }
       const uint32_t next_lds = lds0 + (buf ^ 1) * kBufBytes;
+      if constexpr (kFp8) {
+        // a partial next page is copied here, whole; the score loop copies full pages
+        if (nps.load && nps.valid_rows < kPage) {
+          issue_fp8_partial(nps, next_lds, wave, lane, scale_lds, f8l);
+          nps.load = 0;
+        }
+      }
       if constexpr (kGather) {
         if (nps.load && nseg == seg && nblk == pf_blk) {
 #pragma unroll
@@ -494,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         if constexpr (kGather) {
           if (nps.load) set_rows();
         }
-        issue_page<kGather>(nps, next_lds, wave, lane, tail_lane_off, grows);
+        issue_page<kGather, kFp8>(nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
         buf ^= 1;
         continue;
       }
@@ -534,14 +677,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         // the cache) then overlaps that MFMA instead of delaying the LDS reads and MFMAs
         // behind it (~1,100 cycles per page less than issuing it first).
         // (gathered pages: the two tail copies follow the loop)
-        const bool part = (s & 1) == 0 && s / 2 < (kGather ? 16 : kPageParts);
+        const bool part = (s & 1) == 0 && s / 2 < (kGather ? 16 : (kFp8 ? kFp8Parts : kPageParts));
         if (s == 0) {
           mfma_s_first(sacc[0], a0, qf[s]);
-          if (part) issue_page_part<kGather>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows);
+          if (part) issue_page_part<kGather, kFp8>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
           mfma_s_first(sacc[1], a1, qf[s]);
         } else if (s + 1 < kKSteps) {
           mfma_s(sacc[0], a0, qf[s]);
-          if (part) issue_page_part<kGather>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows);
+          if (part) issue_page_part<kGather, kFp8>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
           mfma_s(sacc[1], a1, qf[s]);
         } else {
           mfma_s(sacc[0], a0, qf[s]);
@@ -554,8 +697,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         // each lane's rows for the two tail copies, now that all 16 row numbers are in
         if (nps.load) {
           set_rows();
-          issue_page_part<kGather>(16, nps, next_lds, wave, lane, tail_lane_off, grows);
-          issue_page_part<kGather>(17, nps, next_lds, wave, lane, tail_lane_off, grows);
+          issue_page_part<kGather, kFp8>(16, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
+          issue_page_part<kGather, kFp8>(17, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
         }
       }
       if (blk + 2 < blk_end) {
@@ -743,15 +886,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
 }  // namespace
 
 hipError_t launch_main_bf16(const Problem& p, hipStream_t stream) {
-  if (p.src_row) {
-    hipLaunchKernelGGL(mla_main_bf16_kernel<true>, dim3(p.num_wg), dim3(kThreads), 0, stream,
-                       (const __bf16*)p.q, (const __bf16*)p.kv, p.src_row, p.num_blocks,
+  if (p.fp8) {
+    hipLaunchKernelGGL((mla_main_bf16_kernel<false, true>), dim3(p.num_wg), dim3(kThreads), 0,
+                       stream, (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
+                       p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
+                       p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
+                       p.part_scale);
+  } else if (p.src_row) {
+    hipLaunchKernelGGL((mla_main_bf16_kernel<true, false>), dim3(p.num_wg), dim3(kThreads), 0,
+                       stream, (const __bf16*)p.q, (const __bf16*)p.kv, p.src_row, p.num_blocks,
                        p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
                        p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
                        p.part_scale);
   } else {
-    hipLaunchKernelGGL(mla_main_bf16_kernel<false>, dim3(p.num_wg), dim3(kThreads), 0, stream,
-                       (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
+    hipLaunchKernelGGL((mla_main_bf16_kernel<false, false>), dim3(p.num_wg), dim3(kThreads), 0,
+                       stream, (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
                        p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
                        p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
                        p.part_scale);

@@ -81,8 +81,9 @@ WORKLOADS = {
 # Quantized latent cache: one 656-byte row per token, 512 latent values as fp8 e4m3 codes
 # (OCP 8-bit float: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities; the
 # all-ones exponent with all-ones mantissa is NaN; largest finite 448), the 64 rope values
-# as bf16, then the row's fp32 scale and 12 bytes of padding.  A latent value is
-# code_value * scale; the rope values are exact.
+# as bf16, then the row's scale (an fp32 power of two, as in the OCP microscaling
+# formats) and 12 bytes of padding.  A latent value is code_value * scale, exact in bf16;
+# the rope values are exact.
 FP8_ROW_BYTES = 656
 FP8_ROPE_OFF = 512
 FP8_SCALE_OFF = 640
@@ -105,11 +106,13 @@ def float_to_e4m3(x: np.ndarray) -> np.ndarray:
 
 def quantize_fp8_cache(kv_bits: np.ndarray) -> np.ndarray:
     """The 656-byte-row fp8 cache of a bf16 cache [blocks, 64, 576] (uint16 bits): per row,
-    scale = max |latent| / 448 (1 for an all-zero row), codes of latent / scale, rope as is."""
+    scale = the smallest power of two >= max |latent| / 448 (1 for an all-zero row), codes
+    of latent / scale, rope as is."""
     x = bf16_bits_to_float32(kv_bits.reshape(-1, 576))
     lat = x[:, :512].astype(np.float64)
     amax = np.abs(lat).max(axis=1)
-    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    scale = np.where(amax > 0, np.exp2(np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0))),
+                     1.0).astype(np.float32)
     codes = float_to_e4m3(lat / scale.astype(np.float64)[:, None])
     out = np.zeros((x.shape[0], FP8_ROW_BYTES), dtype=np.uint8)
     out[:, :512] = codes

@@ -218,8 +218,9 @@ def e4m3_value(codes: np.ndarray) -> np.ndarray:
 
 def fp8_rows(rows: np.ndarray) -> np.ndarray:
     """Float64 [..., 576] rows of a quantized cache stored as 656-byte rows: 512 e4m3
-    latent codes times the row's fp32 scale (bytes 640..643), then the 64 bf16 rope
-    values (bytes 512..639)."""
+    latent codes times the row's fp32 scale (bytes 640..643; the format takes powers of
+    two, but any value is decoded as written), then the 64 bf16 rope values (bytes
+    512..639)."""
     r = np.ascontiguousarray(rows, dtype=np.uint8)
     lead = r.shape[:-1]
     r = r.reshape(-1, r.shape[-1])
