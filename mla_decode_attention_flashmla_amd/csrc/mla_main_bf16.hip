@@ -345,25 +345,34 @@ __device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr
 }
 
 // fp8 pages: widen this wave's 8 row pairs from e4m3 codes to the bf16 main layout in
-// place.  One ds_read_b128 per lane reads 16 codes (lanes 0..31: row 2p, lanes 32..63:
-// row 2p+1) before any lane writes, so row 2p's bf16 may overwrite row 2p+1's codes.
-// The hardware conversion applies the row's scale, a power of two, exactly.
+// place.  Every pair's codes (lanes 0..31: row 2p, lanes 32..63: row 2p+1, 16 codes per
+// lane) and scale are read before any lane writes, so row 2p's bf16 may overwrite the
+// pair's codes and the reads are not serialized behind the writes.  A wave touches only
+// the rows and the scale area its own copies filled.  The hardware conversion applies
+// the row's scale, a power of two, exactly.
 __device__ __forceinline__ void fp8_convert(uint32_t page_lds, uint32_t scale_lds, int wave,
                                             int lane) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   typedef __attribute__((address_space(3))) float lds_f32;
+  u32x4 c[8];
+  float sc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int p = 8 * wave + i;
     const int row = 2 * p + (lane >> 5);
-    const u32x4 c = *(const lds_u32x4*)(uintptr_t)(page_lds + main_row(2 * p) + 16u * lane);
-    const float sc = *(const lds_f32*)(uintptr_t)(scale_lds + (row >> 4) * 256 + (row & 15) * 4);
+    c[i] = *(const lds_u32x4*)(uintptr_t)(page_lds + main_row(2 * p) + 16u * lane);
+    sc[i] = *(const lds_f32*)(uintptr_t)(scale_lds + (row >> 4) * 256 + (row & 15) * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = 8 * wave + i;
+    const int row = 2 * p + (lane >> 5);
     uint32_t o[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], sc, false));
-      o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], sc, true));
+      o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i][k], sc[i], false));
+      o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i][k], sc[i], true));
     }
     const uint32_t dst = page_lds + main_row(row) + 32u * (lane & 31);
     *(lds_u32x4*)(uintptr_t)dst = (u32x4){o[0], o[1], o[2], o[3]};
@@ -596,13 +605,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         has_next = nseg <= seg_last;
       }
       wait_dma();
-      __syncthreads();
       if constexpr (kFp8) {
-        // widen the page's codes to bf16 before any wave reads it or copies the next
-        // page's scales over this one's
+        // each wave widens the rows its own copies filled (no barrier needed before), and
+        // the barrier after it publishes the page and ends every wave's previous page
         fp8_convert(lds0 + buf * kBufBytes, scale_lds, wave, lane);
-        __syncthreads();
       }
+      __syncthreads();
       PageSrc nps;
       nps.load = 0;
       if (has_next) {
