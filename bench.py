@@ -243,7 +243,7 @@ def run_append(args):
 
 def run_fp8(args):
     """Decode over an fp8 latent cache (656-byte rows: fp8 e4m3 latent codes, bf16 rope,
-    fp32 row scale): one mla_decode_fp8_fwd call (dequantize, scheduler, main kernel,
+    fp32 row scale): one mla_decode_fp8_fwd call (scheduler, main kernel over fp8 pages,
     combine).  Algorithmic bytes: each row read once in its 656-byte form, plus Q, O,
     LSE and the tables; flops as for bf16 decode."""
     import numpy as np
@@ -302,7 +302,7 @@ def run_fp8(args):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
     # the dequantize pass and the decode share the work, so the roofline covers the call
-    roof["kernel"] = "mla_decode_fp8_fwd (dequantize, scheduler, main, combine)"
+    roof["kernel"] = "mla_decode_fp8_fwd (scheduler, main over fp8 pages, combine)"
     roof["kernel_us"] = ms_step * 1e3
     res = {
         "metric": METRIC, "value": 100.0 * t_roof / step_s, "unit": "% of roofline",
