@@ -1,13 +1,16 @@
 """GPU parity of MLA decode over a quantized (fp8) latent cache against the oracle.
 
 The cache rows are 656 bytes: 512 fp8 e4m3 latent codes, 64 bf16 rope values and the
-row's fp32 scale.  The oracle dequantizes exactly (fp64); the GPU path writes each
-latent value as bf16 (value * scale, rounded to nearest even) and decodes in bf16, so the
-bar is the bf16 tolerance.  Covered: ragged lengths around block boundaries, causal
-multi-token queries, several row groups, forced splits, a block number outside the pool
-(status bit, NaN for that sequence only) and the full 64 x 8K workload on sampled
-sequences.
+row's fp32 scale, a power of two.  The oracle dequantizes exactly (fp64); the GPU path
+widens each page to bf16 in LDS, which is exact for such scales, and decodes in bf16,
+so the bar is the bf16 tolerance.  Covered: ragged lengths around block boundaries,
+causal multi-token queries, several row groups, forced splits, a block number outside
+the pool (status bit, NaN for that sequence only), the full 64 x 8K workload on sampled
+sequences, and bit-for-bit agreement with the bf16 path over a cache that holds the
+dequantized rows.
 """
+
+import functools
 
 import numpy as np
 import pytest
@@ -17,7 +20,7 @@ from mla_decode_attention_flashmla_amd import binding as B
 from mla_decode_attention_flashmla_amd import inputs as I
 from oracle import mla_oracle as O
 
-from gpu_util import announce, check
+from gpu_util import announce, check, run
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +38,12 @@ def run_fp8(d, num_workgroups=None):
     status = B.read_status(plan)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy(), status
+
+
+@functools.lru_cache(maxsize=1)
+def full_workload():
+    """The full 64 x 8K fp8 workload, built once for the tests that use it."""
+    return I.make_fp8_workload(I.FP8_WORKLOADS["fp8_b64_l8192"])
 
 
 def oracle(d, batches=None):
@@ -77,10 +86,51 @@ def test_fp8_bad_block_flags_only_its_sequence():
 
 def test_fp8_full_size_workload():
     w = I.FP8_WORKLOADS["fp8_b64_l8192"]
-    d = I.make_fp8_workload(w)
+    d = full_workload()
     batches = I.sample_sequences(w.batch, 6, w.seed)
     announce(f"fp8 full size, sampled sequences {batches.tolist()}")
     out, lse, status = run_fp8(d)
     assert status == 0 and np.isfinite(out).all() and np.isfinite(lse).all()
     ref_o, ref_l = oracle(d, batches=batches)
     check(out, lse, ref_o, ref_l, "bf16", batches=batches, what="fp8 full size")
+
+
+def exact_bf16_cache(kv_fp8, chunk=256):
+    """bf16 bit patterns of every dequantized row (the oracle's exact fp64 decoding, in
+    chunks of blocks); asserts that bf16 holds each value exactly."""
+    bits = np.empty(kv_fp8.shape[:2] + (576,), dtype=np.uint16)
+    for i in range(0, kv_fp8.shape[0], chunk):
+        x = O.fp8_rows(kv_fp8[i:i + chunk])
+        b = I.float32_to_bf16_bits(x.astype(np.float32))
+        assert np.array_equal(I.bf16_bits_to_float32(b).astype(np.float64), x)
+        bits[i:i + chunk] = b
+    return bits
+
+
+EQUAL = [
+    # heads, s_q, causal, seqlens (None: the full workload), workgroups
+    (128, 2, True, [2, 130, 1000, 64, 65], 40),
+    (128, 1, False, None, None),
+]
+
+
+@pytest.mark.parametrize("heads,s_q,causal,lens,nwg", EQUAL)
+def test_fp8_equals_bf16_path_on_widened_cache(heads, s_q, causal, lens, nwg):
+    """The widening is exact, so over a bf16 cache holding the dequantized rows the bf16
+    path computes on the same values, with the same plan and the same products: O and
+    LSE agree bit for bit, for every sequence of the full workload too."""
+    if lens is None:
+        d = full_workload()
+    else:
+        w = I.Workload("fp8eq", len(lens), s_q, heads, max(lens), "bf16", 192,
+                       causal=causal, ragged=True, seed=90 + s_q)
+        d = I.make_fp8_workload(w, seqlens=lens)
+    announce(f"fp8 vs bf16 path, H={heads} s_q={s_q} causal={causal} lens={lens} nwg={nwg}")
+    d16 = dict(d)
+    d16["kv_cache"] = exact_bf16_cache(d["kv_cache"])
+    out8, lse8, st8 = run_fp8(d, nwg)
+    out16, lse16, st16, _ = run(d16, num_workgroups=nwg)
+    assert st8 == 0 and st16 == 0
+    assert np.isfinite(out8).all() and np.isfinite(lse8).all()
+    assert np.array_equal(out8, out16), float(np.abs(out8 - out16).max())
+    assert np.array_equal(lse8, lse16), float(np.abs(lse8 - lse16).max())
