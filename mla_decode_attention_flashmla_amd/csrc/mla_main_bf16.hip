@@ -345,38 +345,48 @@ __device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr
 }
 
 // fp8 pages: widen this wave's 8 row pairs from e4m3 codes to the bf16 main layout in
-// place.  Every pair's codes (lanes 0..31: row 2p, lanes 32..63: row 2p+1, 16 codes per
-// lane) and scale are read before any lane writes, so row 2p's bf16 may overwrite the
-// pair's codes and the reads are not serialized behind the writes.  A wave touches only
-// the rows and the scale area its own copies filled.  The hardware conversion applies
-// the row's scale, a power of two, exactly.
+// place.  Lane l works on row 2p + l/32: with i = l%32 it reads codes 8i..8i+7 and
+// 256+8i..256+8i+7 (two 8-byte reads) and writes their bf16 values at columns 8i and
+// 256+8i, so every read and write is contiguous across the lanes of a row (no LDS bank
+// conflicts).  Every pair's codes and scale are read before any lane writes, so row
+// 2p's bf16 may overwrite the pair's codes and the reads are not serialized behind the
+// writes.  A wave touches only the rows and the scale area its own copies filled.  The
+// hardware conversion applies the row's scale, a power of two, exactly.
 __device__ __forceinline__ void fp8_convert(uint32_t page_lds, uint32_t scale_lds, int wave,
                                             int lane) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   typedef __attribute__((address_space(3))) float lds_f32;
-  u32x4 c[8];
+  const uint32_t half = (uint32_t)(lane >> 5), il = (uint32_t)(lane & 31);
+  u32x2 lo[8], hi[8];
   float sc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int p = 8 * wave + i;
-    const int row = 2 * p + (lane >> 5);
-    c[i] = *(const lds_u32x4*)(uintptr_t)(page_lds + main_row(2 * p) + 16u * lane);
+    const int row = 2 * p + (int)half;
+    const uint32_t src = page_lds + main_row(2 * p) + 512u * half + 8u * il;
+    lo[i] = *(const lds_u32x2*)(uintptr_t)src;
+    hi[i] = *(const lds_u32x2*)(uintptr_t)(src + 256);
     sc[i] = *(const lds_f32*)(uintptr_t)(scale_lds + (row >> 4) * 256 + (row & 15) * 4);
   }
+  auto widen8 = [](u32x2 c, float s) __attribute__((always_inline)) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], s, false));
+      o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[k], s, true));
+    }
+    return o;
+  };
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int p = 8 * wave + i;
-    const int row = 2 * p + (lane >> 5);
-    uint32_t o[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      o[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i][k], sc[i], false));
-      o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i][k], sc[i], true));
-    }
-    const uint32_t dst = page_lds + main_row(row) + 32u * (lane & 31);
-    *(lds_u32x4*)(uintptr_t)dst = (u32x4){o[0], o[1], o[2], o[3]};
-    *(lds_u32x4*)(uintptr_t)(dst + 16) = (u32x4){o[4], o[5], o[6], o[7]};
+    const int row = 2 * p + (int)half;
+    const uint32_t dst = page_lds + main_row(row) + 16u * il;
+    *(lds_u32x4*)(uintptr_t)dst = widen8(lo[i], sc[i]);
+    *(lds_u32x4*)(uintptr_t)(dst + 512) = widen8(hi[i], sc[i]);
   }
 }
 
