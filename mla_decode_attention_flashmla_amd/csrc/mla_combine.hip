@@ -15,8 +15,8 @@
 namespace mla {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 4;  // 64 threads per row, 8 columns per thread
+constexpr int kThreads = 64 * kRowsPerBlock;
 constexpr int kMaxSplitsLds = 1024;
 constexpr int kBatch = 4;         // parts whose O loads are in flight together
 

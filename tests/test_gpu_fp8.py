@@ -4,7 +4,7 @@ The cache rows are 656 bytes: 512 fp8 e4m3 latent codes, 64 bf16 rope values and
 row's fp32 scale, a power of two.  The oracle dequantizes exactly (fp64); the GPU path
 widens each page to bf16 in LDS, which is exact for such scales, and decodes in bf16,
 so the bar is the bf16 tolerance.  Covered: ragged lengths around block boundaries,
-causal multi-token queries, several row groups, forced splits, a block number outside
+causal multi-token queries and 16-token chunks, several row groups, forced splits, a block number outside
 the pool (status bit, NaN for that sequence only), the full 64 x 8K workload on sampled
 sequences, and bit-for-bit agreement with the bf16 path over a cache that holds the
 dequantized rows.
@@ -57,6 +57,7 @@ SMALL = [
     (128, 2, True, [2, 130, 1000], 40),          # causal pair, forced splits
     (64, 1, False, [300, 5, 129], 7),            # few workgroups: long ranges
     (48, 3, True, [200, 3, 90], None),           # 144 rows: two row groups
+    (128, 16, True, [16, 700, 1500], 24),        # 16-token causal chunks, 16 row groups
 ]
 
 
