@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -340,10 +341,15 @@ def run_fp8(args):
 
 
 def kernel_hash():
+    """Hash of the main kernel's code: its sources with comments and whitespace removed,
+    so an edit to comments alone keeps a counter record valid."""
     h = hashlib.sha256()
     for f in ("mla_main_bf16.hip", "mla_internal.h", "mla_oacc_asm.h"):
-        with open(os.path.join(os.path.dirname(KERNEL_SRC), f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(os.path.dirname(KERNEL_SRC), f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

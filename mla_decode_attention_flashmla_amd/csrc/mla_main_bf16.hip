@@ -34,6 +34,16 @@
 // O is only rescaled when a page raises some row's max by more than that, so
 // exp2 arguments stay <= 8 and the rescale (three VALU ops per O element) is rare.
 //
+// Page sources (template parameters, one instantiation each):
+//   paged     a 64-token block of the bf16 cache, named by the block table;
+//   kGather   64 rows read one by one from the bf16 pool by their pool row numbers (the
+//             rows a sparse selection picked, listed by the index kernel);
+//   kFp8      a block of 656-byte rows (e4m3 latent codes, bf16 rope, a power-of-two
+//             scale), copied as is and widened to the bf16 layout below in LDS before
+//             the page's scores.
+// Every source ends in the same LDS layout, so the products, the softmax and the
+// epilogue are shared.
+//
 // LDS page layout (77824 bytes, two pages double-buffered), for 64 banks of 4 bytes:
 //   main region  columns 0..511 of row r (1024 bytes) at 1088*r + 16*((r>>2)&3).
 //                Row starts are 64*(r&3) + 16*((r>>2)&3) modulo 256 bytes, so the
