@@ -225,27 +225,32 @@ def test_stale_plan_is_flagged():
     assert np.isnan(out[1].cpu().numpy()).all() and np.isnan(lse[1].cpu().numpy()).all()
 
 
-def test_scheduler_partition_invariants():
+# (sequences, query tokens): 74 segments (the scheduler's block-wide path), exactly 64
+# and 33 (its one-wave path)
+@pytest.mark.parametrize("batch,s_q", [(37, 2), (32, 2), (33, 1)])
+def test_scheduler_partition_invariants(batch, s_q):
     """Every block of every segment is covered by exactly one workgroup range; part counts
     and partial slots are consistent."""
-    w = I.Workload("sch", 37, 2, 128, 5000, "bf16", 192, causal=True, ragged=True, seed=43)
+    groups = s_q  # 128 heads: one 128-row group per query token
+    w = I.Workload("sch", batch, s_q, 128, 5000, "bf16", 192, causal=s_q > 1, ragged=True,
+                   seed=43)
     d = I.make_workload(w)
     d["seqlens"][5] = 2
     t = to_device(d)
     for nwg, minb in ((256, 0), (256, 1), (13, 3), (1000, 1), (1000, 0), (7, 0), (60, 0),
                       (100, 0)):
-        announce(f"scheduler nwg={nwg} min_split={minb}")
-        plan = B.alloc_plan(37, 2, 128, True, t["table"].shape[1], nwg)
+        announce(f"scheduler batch={batch} s_q={s_q} nwg={nwg} min_split={minb}")
+        plan = B.alloc_plan(batch, s_q, 128, s_q > 1, t["table"].shape[1], nwg)
         B.get_split_metadata(t["lens"], plan, minb)
         torch.cuda.synchronize()
         m = plan.meta.cpu().numpy()
         nseg = m[7]
         wg = m[32:32 + 8 * nwg].reshape(nwg, 8)
         seg = m[32 + 8 * nwg:32 + 8 * nwg + 8 * nseg].reshape(nseg, 8)
-        assert nseg == 37 * 2 and m[6] == 0
+        assert nseg == batch * groups and m[6] == 0
         T, n, c_al = int(m[9]), int(m[10]), int(m[13])
         lens = d["seqlens"]
-        nb = np.repeat((lens + 63) // 64, 2)
+        nb = np.repeat((lens + 63) // 64, groups)
         assert np.array_equal(seg[:, 0], nb)
         c_min = -(-T // nwg)
         if minb == 0 and c_al > 0:
