@@ -34,21 +34,29 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
   const int nwg = gridDim.x;
   int slot = blockIdx.x;
   if ((nwg & 7) == 0) slot = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  if (meta[H_MAGIC] != kMagic || meta[H_BATCH] != batch || meta[H_SQ] != s_q ||
-      meta[H_HEADS] != heads || meta[H_CAUSAL] != causal || meta[H_NUM_WG] != nwg ||
-      meta[H_MAX_BLOCKS] != max_blocks) {
+  // The header and this slot's row are read together (one round trip): the row lies
+  // inside the buffer the host validated for these sizes, and nothing read from it is
+  // used before the header check.
+  const int32_t* wrow = meta + kHdrWords + (size_t)slot * kWgWords;
+  const int32_t* segt = meta + kHdrWords + (size_t)kWgWords * nwg;
+  const int h_magic = meta[H_MAGIC], h_batch = meta[H_BATCH], h_sq = meta[H_SQ];
+  const int h_heads = meta[H_HEADS], h_causal = meta[H_CAUSAL], h_nwg = meta[H_NUM_WG];
+  const int h_maxb = meta[H_MAX_BLOCKS], groups = meta[H_NUM_GROUPS];
+  const int seg_first = wrow[W_SEG_BEGIN], blk_first = wrow[W_BLK_BEGIN];
+  const int seg_last = wrow[W_SEG_END], blk_last_end = wrow[W_BLK_END];
+  const int split_first = wrow[W_FIRST_SPLIT];
+  // all of them loaded here, before the first test (kept from being sunk past it)
+  asm volatile("" ::"s"(h_magic), "s"(h_batch), "s"(h_sq), "s"(h_heads), "s"(h_causal),
+               "s"(h_nwg), "s"(h_maxb), "s"(groups), "s"(seg_first), "s"(blk_first),
+               "s"(seg_last), "s"(blk_last_end), "s"(split_first));
+  const bool plan_ok = (h_magic == kMagic) & (h_batch == batch) & (h_sq == s_q) &
+                       (h_heads == heads) & (h_causal == causal) & (h_nwg == nwg) &
+                       (h_maxb == max_blocks);
+  if (!plan_ok) {
     if (tid == 0) atomicOr(&meta[H_STATUS], MLA_STATUS_PLAN_MISMATCH);
     return;
   }
-  const int32_t* wrow = meta + kHdrWords + (size_t)slot * kWgWords;
-  const int32_t* segt = meta + kHdrWords + (size_t)kWgWords * nwg;
-  const int seg_first = wrow[W_SEG_BEGIN];
   if (seg_first < 0) return;
-  const int blk_first = wrow[W_BLK_BEGIN];
-  const int seg_last = wrow[W_SEG_END];
-  const int blk_last_end = wrow[W_BLK_END];
-  const int split_first = wrow[W_FIRST_SPLIT];
-  const int groups = meta[H_NUM_GROUPS];
   const int M = s_q * heads;
   // ranges read from the plan stay inside this call's tables even if the plan is corrupt
   const int nseg = batch * ((M + kGroupRows - 1) / kGroupRows);
