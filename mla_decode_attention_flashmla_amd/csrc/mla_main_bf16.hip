@@ -568,6 +568,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     bool bad_block = bad_block_next;
     bad_block_next = false;
     const bool mismatch = sload(seqlens + b) != L;
+    // read now, used by the epilogue: the loads complete while the pages run
+    const int seg_nsplit = sload(segt + (size_t)seg * kSegWords + S_NSPLIT);
+    const int seg_slot = sload(segt + (size_t)seg * kSegWords + S_SLOT);
 
     // this lane's query row
     const int row_in_group = wave * 32 + l32;
@@ -828,7 +831,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     const bool bad = bad_block || mismatch;
     if (wave_active) {
-      const int nsplit = sload(segt + (size_t)seg * kSegWords + S_NSPLIT);
+      const int nsplit = seg_nsplit;
       const bool whole = nsplit == 1;
       const float l_tot = swap_halves_sum(l_run);
       float inv, lse_v;
@@ -865,7 +868,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         // significant bits and none overflows; the combine multiplies the scale back.
         // Half the bytes of fp32 partials, written here and read again by the combine.
         const int split = seg == seg_first ? split_first : 0;
-        const size_t slot_i = (size_t)sload(segt + (size_t)seg * kSegWords + S_SLOT) + split;
+        const size_t slot_i = (size_t)seg_slot + split;
         float amax = 0.f;
 #pragma unroll
         for (int ct = 0; ct < kCTiles; ++ct) {
