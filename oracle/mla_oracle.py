@@ -78,8 +78,20 @@ def check_lengths(seqlens: np.ndarray, block_table: np.ndarray, s_q: int, causal
             raise ValueError(f"sequence {b}: causal length {L} shorter than {s_q} queries")
 
 
+def weights_and_lse(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Scaled scores s[h, j] = scale * <q_h, K_j> of query rows [H, 576] against keys
+    [n, 576] (n >= 1), their log-sum-exp LSE[h] = ln sum_j exp(s[h, j]) (taken as
+    m + ln sum_j exp(s - m) with m the row max, so no term overflows), and the weights
+    p[h, j] = exp(s[h, j] - LSE[h]).  Returns (p [H, n], LSE [H])."""
+    s = scale * (q_rows @ keys.T)                      # [H, n]
+    m = s.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    return np.exp(s - lse[:, None]), lse
+
+
 def attend_one(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """Attention of query rows [H, 576] over keys [n, 576] (V = keys[:, :512]), float64.
+    """Attention of query rows [H, 576] over keys [n, 576] (V = keys[:, :512]), float64:
+    O[h] = sum_j p[h, j] * V_j with the weights of ``weights_and_lse``.
 
     Returns (O [H, 512], LSE [H]).  n = 0 gives O = 0 and LSE = -inf.
     """
@@ -87,13 +99,8 @@ def attend_one(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> Tuple[np.n
     n = keys.shape[0]
     if n == 0:
         return np.zeros((H, D_V)), np.full(H, -np.inf)
-    s = scale * (q_rows @ keys.T)                      # [H, n]
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    tot = e.sum(axis=1, keepdims=True)
-    lse = (m + np.log(tot))[:, 0]
-    o = (e / tot) @ keys[:, :D_V]
-    return o, lse
+    p, lse = weights_and_lse(q_rows, keys, scale)
+    return p @ keys[:, :D_V], lse
 
 
 def mla_decode(q, kv_cache, block_table, seqlens, scale, causal=False, dtype="bf16",
@@ -231,11 +238,30 @@ def fp8_rows(rows: np.ndarray) -> np.ndarray:
     return out.reshape(*lead, D_QK)
 
 
+FP8_MIN_SCALE_EXP = -117
+FP8_MAX_SCALE_EXP = 119
+
+
+def fp8_scale_in_format(scales: np.ndarray) -> np.ndarray:
+    """True where a row scale belongs to the quantized format: a power of two 2^k with
+    -117 <= k <= 119.  Then every e4m3 code value (magnitudes 2^-9 .. 448, or 0) times
+    the scale is zero or a normal bf16 number, i.e. the dequantized row is exact in
+    bf16; other scales (not a power of two, outside the range, <= 0, NaN, inf) are not
+    rows of the format."""
+    s = np.asarray(scales, dtype=np.float64)
+    ok = np.isfinite(s) & (s > 0)
+    man, ex = np.frexp(np.where(ok, s, 1.0))           # s = man * 2^ex, man in [0.5, 1)
+    k = ex - 1
+    return ok & (man == 0.5) & (k >= FP8_MIN_SCALE_EXP) & (k <= FP8_MAX_SCALE_EXP)
+
+
 def mla_decode_fp8(q, kv_fp8, block_table, seqlens, scale, causal=False,
                    batches: Iterable[int] | None = None):
     """MLA decode over a quantized latent cache [blocks, 64, 656] bytes: the same
     definition as ``mla_decode`` with every key/value row dequantized exactly (fp64)
-    by ``fp8_rows``; q holds bf16 bit patterns."""
+    by ``fp8_rows``; q holds bf16 bit patterns.  A sequence one of whose rows [0, L_b)
+    has a scale outside the format (``fp8_scale_in_format``) is an invalid input, as an
+    invalid length is: ValueError."""
     q = np.asarray(q)
     B, s_q, H, D = q.shape
     if D != D_QK or kv_fp8.shape[1:] != (PAGE, 656):
@@ -247,7 +273,11 @@ def mla_decode_fp8(q, kv_fp8, block_table, seqlens, scale, causal=False,
     lse = np.full((B, s_q, H), np.nan)
     for b in (range(B) if batches is None else batches):
         L = int(seqlens[b])
-        keys = fp8_rows(gather_rows(kv_fp8, block_table, b, L))
+        raw = gather_rows(kv_fp8, block_table, b, L)
+        row_scales = np.ascontiguousarray(raw[:, 640:644]).view(np.float32)[:, 0]
+        if not fp8_scale_in_format(row_scales).all():
+            raise ValueError(f"sequence {b}: a row scale outside the quantized format")
+        keys = fp8_rows(raw)
         qb = widen(q[b], "bf16")
         for t in range(s_q):
             n = visible_keys(L, s_q, t, causal)
@@ -256,11 +286,9 @@ def mla_decode_fp8(q, kv_fp8, block_table, seqlens, scale, causal=False,
 
 
 def softmax_weights(q_rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
-    """The attention weights p[h, j] = exp(s_j - LSE_h) the outputs are built from."""
-    s = scale * (q_rows @ keys.T)
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    return e / e.sum(axis=1, keepdims=True)
+    """The attention weights p[h, j] = exp(s_j - LSE_h) that ``attend_one`` builds its
+    outputs from (the same function, so a pin on them pins the outputs' weights)."""
+    return weights_and_lse(q_rows, keys, scale)[0]
 
 
 def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):
@@ -292,7 +320,9 @@ def brute_force(q_list, keys_list, scale: float, causal: bool, s_q: int):
     for b, rows in enumerate(keys_list):
         ob, lb = [], []
         for t in range(s_q):
-            n = visible_keys(len(rows), s_q, t, causal)
+            # the causal bound written out (not through visible_keys), so this loop pins it:
+            # the s_q queries are the sequence's last s_q positions, t sees keys 0 .. L-s_q+t
+            n = len(rows) - s_q + 1 + t if causal else len(rows)
             ot, lt = [], []
             for qh in q_list[b][t]:
                 if n == 0:

@@ -156,6 +156,30 @@ def test_weights_sum_to_one_and_lse_closed_form():
         assert abs(lse[h] - math.log(math.fsum(math.exp(x) for x in s))) < 1e-12
 
 
+def test_weights_depend_on_the_scale_as_the_definition_says():
+    """P3': two keys whose raw dot products with q are 0 and 1, scale ln 3: the scaled
+    scores are 0 and ln 3, so the weights are exactly 1/4 and 3/4, LSE = ln 4 and
+    O = V_0/4 + 3 V_1/4.  A dropped or doubled scale gives other weights (1/(1+e), or
+    1/10), so this pins the scale's use, which Sum(p) = 1 and the argmax cannot."""
+    q = np.zeros((1, 576))
+    q[0, 3] = 1.0
+    keys = np.zeros((2, 576))
+    keys[1, 3] = 1.0
+    keys[0, 10], keys[1, 10] = 8.0, 4.0         # V_0[10] = 8, V_1[10] = 4
+    keys[0, 500], keys[1, 500] = -2.0, 6.0
+    scale = math.log(3.0)
+    p = O.softmax_weights(q, keys, scale)
+    np.testing.assert_allclose(p, [[0.25, 0.75]], rtol=0, atol=1e-15)
+    o, lse = O.attend_one(q, keys, scale)
+    assert abs(lse[0] - math.log(4.0)) < 1e-15
+    np.testing.assert_allclose(o[0, 10], 0.25 * 8.0 + 0.75 * 4.0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[0, 500], 0.25 * -2.0 + 0.75 * 6.0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[0, 3], 0.75, rtol=0, atol=1e-15)   # V_1[3] = 1 (the key)
+    assert np.count_nonzero(o[0]) == 3
+    # attend_one's O is built from exactly these weights
+    np.testing.assert_array_equal(o, p @ keys[:, :512])
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_brute_force_tiny(causal):
     """P5: pure-Python loops (fsum, math.exp) over dense keys agree to 1e-12."""
@@ -496,3 +520,35 @@ def test_fp8_decode_equals_bf16_decode_when_quantization_is_exact():
     ob, lb = O.mla_decode(d["q"], kv, d["block_table"], d["seqlens"], d["scale"], True)
     np.testing.assert_allclose(o8, ob, rtol=0, atol=1e-13)
     np.testing.assert_allclose(l8, lb, rtol=0, atol=1e-13)
+
+
+def test_fp8_scales_of_the_format():
+    """The format's row scales are the powers of two 2^k, -117 <= k <= 119: then every
+    code value (2^-9 .. 448 in magnitude) times the scale is a normal bf16 number."""
+    ok = [2.0 ** -117, 2.0 ** -8, 0.25, 1.0, 2.0, 2.0 ** 119]
+    bad = [2.0 ** -118, 2.0 ** 120, 0.75, 3.0, -1.0, -0.25, 0.0, -0.0, np.nan, np.inf,
+           1.0 + 2.0 ** -23, 2.0 ** -126, 2.0 ** 127]
+    assert O.fp8_scale_in_format(np.array(ok, np.float32)).all()
+    assert not O.fp8_scale_in_format(np.array(bad, np.float32)).any()
+    # the bound is where the format stays exact and normal in bf16: smallest subnormal
+    # code 2^-9 times 2^-117 is 2^-126, the smallest normal; 448 * 2^119 < 2^128
+    assert 2.0 ** -9 * 2.0 ** -117 == 2.0 ** -126 and 448 * 2.0 ** 119 < 2.0 ** 128
+    assert 448 * 2.0 ** 120 > float(np.finfo(np.float32).max)
+
+
+def test_fp8_row_scale_outside_the_format_is_an_invalid_input():
+    """A sequence with a row scale outside the format is rejected (as an invalid length
+    is); a bad scale in a row past the sequence's length is never read."""
+    w = I.Workload("fp8bad", 2, 1, 4, 100, "bf16", 192, seed=19)
+    d = I.make_fp8_workload(w, seqlens=[100, 70])
+    kv = d["kv_cache"].copy()
+    blk = int(d["block_table"][0, 1])
+    kv[blk, 36, 640:644] = np.array([0.75], np.float32).view(np.uint8)  # row 100 - 64 = 36: past L
+    o, l = O.mla_decode_fp8(d["q"], kv, d["block_table"], d["seqlens"], d["scale"])
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    kv[blk, 35, 640:644] = np.array([0.75], np.float32).view(np.uint8)      # row 99: inside
+    with pytest.raises(ValueError):
+        O.mla_decode_fp8(d["q"], kv, d["block_table"], d["seqlens"], d["scale"])
+    o1, l1 = O.mla_decode_fp8(d["q"], kv, d["block_table"], d["seqlens"], d["scale"],
+                              batches=[1])
+    assert np.isfinite(o1[1]).all() and np.isnan(o1[0]).all()
