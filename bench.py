@@ -141,11 +141,7 @@ def run_sparse(args):
     }
     if not args.no_cpu_baseline:
         from oracle import mla_oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            cores = os.cpu_count() or 1
+        cores = blas_threads()
         done = []
         c0 = time.perf_counter()
         for b in range(Bn):
@@ -161,7 +157,7 @@ def run_sparse(args):
             "kind": "oracle",
             "sample": f"{len(done)} of {Bn} sequences, fp64 numpy, {el:.1f} s; scaled to the "
                       "whole batch",
-            "seconds_per_step_est": t_full, "tflops": flops / t_full / 1e12,
+            "seconds_per_step_est": t_full, "tflops": flops / t_full / 1e12, **host_info(),
         }
     print(json.dumps(res), flush=True)
 
@@ -332,11 +328,82 @@ def run_fp8(args):
         t_full = el * Bn / len(done)
         res["cpu_baseline"] = {
             "value": 100.0 * t_roof / t_full, "unit": "% of roofline",
-            "cores": os.cpu_count() or 1, "kind": "oracle",
+            "cores": blas_threads(), "kind": "oracle", **host_info(),
             "sample": f"{len(done)} of {Bn} sequences, fp64 numpy, {el:.1f} s; scaled to the "
                       "whole batch",
             "seconds_per_step_est": t_full,
         }
+    print(json.dumps(res), flush=True)
+
+
+def run_hbm_ceiling(args):
+    """What reads alone reach on this device (libmla_probe.so): a grid-stride stream over
+    2 GiB, and the main kernel's page-copy structure without its compute (one workgroup
+    per compute unit, 72 KiB pages in a seeded random order, copied into LDS) over 2 GiB
+    and over the 64 x 8K workload's 8192-page pool.  Prints one JSON line of GB/s."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_flashmla_amd import binding as B
+
+    lib_path = os.path.join(ROOT, "mla_decode_attention_flashmla_amd", "libmla_probe.so")
+    if not os.path.exists(lib_path):
+        raise SystemExit(f"{lib_path} is missing: build first")
+    lib = ctypes.CDLL(lib_path)
+    c_p, c_sz, c_int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.mla_probe_stream_read.argtypes = [c_p, c_sz, c_int, c_int, c_p, c_p]
+    lib.mla_probe_page_read.argtypes = [c_p, c_int, c_int, c_p, c_int, c_int, c_p, c_p]
+    dev = torch.device("cuda", 0)
+    cus = B.device_workgroups(0)
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    sink = torch.zeros(16 * cus * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    res = {"metric": "HBM read ceiling", "unit": "GB/s", "device_cus": cus, "results": []}
+    for nt in (0, 1):
+        for wgs in (4 * cus, 8 * cus, 16 * cus):
+            def f(nt=nt, wgs=wgs):
+                rc = lib.mla_probe_stream_read(buf.data_ptr(), nbytes, nt, wgs, sink.data_ptr(), sp)
+                assert rc == 0, rc
+            t = timed(f, args.steps)
+            res["results"].append({"kind": "stream", "nontemporal": nt, "workgroups": wgs,
+                                   "bytes": nbytes, "us": t * 1e6, "gbs": nbytes / t / 1e9})
+            print(f"[ceiling] {res['results'][-1]}", file=sys.stderr, flush=True)
+    rng = np.random.default_rng(5)
+    for unit, nbuf in ((73728, 2), (36864, 3), (36864, 4), (16384, 8)):
+        for pool_bytes, name in ((nbytes, "2GiB"), (8192 * 73728, "gate_pool")):
+            nunits = pool_bytes // unit
+            order_np = rng.permutation(nunits).astype(np.int32)
+            # every block index names a block inside the buffer (checked here, on the host)
+            assert order_np.min() >= 0 and (int(order_np.max()) + 1) * unit <= nbytes
+            order = torch.from_numpy(order_np).to(dev)
+            read = nunits * unit
+
+            def g(unit=unit, nbuf=nbuf, order=order, nunits=nunits):
+                rc = lib.mla_probe_page_read(buf.data_ptr(), unit, nbuf, order.data_ptr(), nunits,
+                                             cus, sink.data_ptr(), sp)
+                assert rc == 0, rc
+            t = timed(g, args.steps)
+            res["results"].append({"kind": "pages_to_lds", "unit_bytes": unit, "buffers": nbuf,
+                                   "pool": name, "workgroups": cus, "bytes": read,
+                                   "us": t * 1e6, "gbs": read / t / 1e9})
+            print(f"[ceiling] {res['results'][-1]}", file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
 
 
@@ -366,28 +433,134 @@ def measured_traffic(workload):
     return t.get("bytes_per_launch")
 
 
+def gpu_clocks():
+    """Current clocks and power of the visible GPUs as rocm-smi reports them (raw strings,
+    keyed by card); None where rocm-smi is missing or fails.  Sampled outside the timed
+    region."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception:  # pragma: no cover - depends on the host
+        return None
+    keep = {}
+    for card, fields in data.items():
+        if not isinstance(fields, dict):
+            continue
+        keep[card] = {k.strip(" :"): v for k, v in fields.items()
+                      if "clock" in k.lower() or "power" in k.lower()}
+    return keep or None
+
+
+def host_info():
+    """The host's CPU model and core counts (for the CPU baseline)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count()
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "cpus_available": avail}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def percentiles(ms):
+    """Median, p10 and p90 (and extremes) of per-step times in microseconds."""
+    import numpy as np
+
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "min": float(a.min()), "max": float(a.max())}
+
+
+def timed_steps(step, steps, stream, flush=None):
+    """Run `steps` steps on `stream` with a HIP event at every step boundary.
+
+    Returns (total_ms, per_step_ms).  Without `flush` the steps run back to back and the
+    total is first event to last.  With `flush` (a callable that writes a large scratch
+    buffer, evicting L2 and the memory-side cache) the flush runs between steps outside
+    the events: each step gets its own event pair and the total is their sum."""
+    import torch
+
+    if flush is None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return ev[0].elapsed_time(ev[-1]), per
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        flush()
+        a[i].record(stream)
+        step()
+        b[i].record(stream)
+    torch.cuda.synchronize()
+    per = [a[i].elapsed_time(b[i]) for i in range(steps)]
+    return sum(per), per
+
+
+def make_flush(dev, mib=1024):
+    """A callable that writes `mib` MiB of scratch on the device (L2 and MALL flush)."""
+    import torch
+
+    buf = torch.empty(mib << 18, dtype=torch.float32, device=dev)
+
+    def flush():
+        buf.fill_(1.0)
+    return flush
+
+
 def cpu_baseline(d, budget_s: float):
     """Time the CPU oracle on whole sequences of the same workload until budget_s is spent."""
     import numpy as np
     from oracle import mla_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = blas_threads()
     w = d["workload"]
+
+    def one(b):
+        O.mla_decode(d["q"][b:b + 1], d["kv_cache"], d["block_table"][b:b + 1],
+                     d["seqlens"][b:b + 1], d["scale"], d["causal"], dtype=w.dtype)
+
     done = []
     t0 = time.perf_counter()
     for b in range(w.batch):
-        O.mla_decode(d["q"], d["kv_cache"], d["block_table"], d["seqlens"], d["scale"],
-                     d["causal"], dtype=w.dtype, batches=[b])
+        one(b)
         done.append(b)
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
+    runs = 1
+    if len(done) == w.batch and el * 3 <= budget_s:
+        # a whole pass fits the budget three times over: best of three passes
+        for _ in range(2):
+            t1 = time.perf_counter()
+            for b in range(w.batch):
+                one(b)
+            el = min(el, time.perf_counter() - t1)
+        runs = 3
     frac = float(d["seqlens"][done].astype(np.int64).sum()) / float(d["seqlens"].astype(np.int64).sum())
-    return el, frac, len(done), cores
+    return el, frac, len(done), cores, runs
 
 
 def main():
@@ -408,6 +581,13 @@ def main():
                          "launch per step costs more than the three launch gaps it removes)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy this many MiB once (counter calibration runs)")
+    ap.add_argument("--flush", action="store_true",
+                    help="write 1 GiB of scratch between timed steps, outside the events, so "
+                         "no step finds the cache in L2 or the 256 MB memory-side cache")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not sample clocks and power with rocm-smi")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="measure the device's read-bandwidth ceiling (probe kernels) instead")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -415,6 +595,9 @@ def main():
               "(the decode runs on a single GPU, with no inter-GPU sharding).", file=sys.stderr)
         sys.exit(2)
 
+    if args.hbm_ceiling:
+        run_hbm_ceiling(args)
+        return
     from mla_decode_attention_flashmla_amd import inputs as I
     if args.workload in I.SPARSE_WORKLOADS:
         run_sparse(args)
@@ -456,8 +639,12 @@ def main():
         B.decode_main(q, kv, table, lens, scale, out, lse, plan)
         B.decode_combine(q, kv, table, lens, scale, out, lse, plan)
 
+    clocks_before = None if args.no_clocks else gpu_clocks()
+    flush = make_flush(dev) if args.flush else None
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
+        if flush:
+            flush()
         step()
     torch.cuda.synchronize()
     if B.read_status(plan) != 0:
@@ -485,30 +672,21 @@ def main():
         torch.cuda.synchronize()
         if B.read_status(plan) != 0:
             raise SystemExit("device status flagged an error (graph replay)")
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        run_step()
-    t1.record(stream)
-    torch.cuda.synchronize()
+    total_ms, per_step = timed_steps(run_step, args.steps, stream, flush)
     wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
     ms_step = total_ms / args.steps
 
-    # the dominant kernel alone: the same number of main-kernel launches back to back
-    # (the plan stays valid), between two events on the stream they are launched on
-    m0 = torch.cuda.Event(enable_timing=True)
-    m1 = torch.cuda.Event(enable_timing=True)
-    m0.record(stream)
-    for _ in range(args.steps):
+    # the dominant kernel alone: the same number of main-kernel launches (the plan stays
+    # valid), each between two events on the stream it is launched on
+    def main_only():
         B.decode_main(q, kv, table, lens, scale, out, lse, plan)
-    m1.record(stream)
-    torch.cuda.synchronize()
-    main_avg_us = m0.elapsed_time(m1) * 1e3 / args.steps
+    main_total_ms, main_per = timed_steps(main_only, args.steps, stream, flush)
+    main_avg_us = main_total_ms * 1e3 / args.steps
     B.decode_combine(q, kv, table, lens, scale, out, lse, plan)
     torch.cuda.synchronize()
+    clocks_after = None if args.no_clocks else gpu_clocks()
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -558,20 +736,26 @@ def main():
         "alg_flops": flops,
         "roofline_us": t_roof * 1e6,
         "wall_s": wall,
+        "step_us": percentiles(per_step),
+        "main_kernel_us": percentiles(main_per),
+        "flush": bool(args.flush),
+        "clocks": {"before_warmup": clocks_before, "after_timing": clocks_after},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (budget {args.cpu_budget}s)", file=sys.stderr,
               flush=True)
-        el, frac, nseq, cores = cpu_baseline(d, args.cpu_budget)
+        el, frac, nseq, cores, runs = cpu_baseline(d, args.cpu_budget)
         t_full = el / frac
+        how = "best of 3 whole passes" if runs == 3 else "one pass"
         res["cpu_baseline"] = {
             "value": 100.0 * t_roof / t_full, "unit": "% of roofline",
             "cores": cores, "kind": "oracle",
-            "sample": f"{nseq} of {Bn} sequences ({frac * 100:.1f}% of the keys), fp64 numpy, "
-                      f"{el:.1f} s; scaled to the whole batch",
+            "sample": f"{nseq} of {Bn} sequences ({frac * 100:.1f}% of the keys), fp64 numpy "
+                      f"with {cores} BLAS threads, {how}, {el:.2f} s; scaled to the whole batch",
             "seconds_per_step_est": t_full,
             "tflops": flops / t_full / 1e12,
+            **host_info(),
         }
     print(json.dumps(res), flush=True)
 

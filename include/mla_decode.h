@@ -75,7 +75,8 @@ extern "C" {
 /* Device status bits (mla_read_status). */
 #define MLA_STATUS_BAD_SEQLEN 1     /* L_b < 0, L_b > 64 * max_blocks_per_seq, or causal L_b < s_q */
 #define MLA_STATUS_BAD_BLOCK 2      /* a block_table entry read was outside [0, num_blocks) */
-#define MLA_STATUS_PLAN_MISMATCH 4  /* plan built for other sizes or other seqlens */
+#define MLA_STATUS_PLAN_MISMATCH 4  /* plan built for other sizes, seqlens, causal flag or table width */
+#define MLA_STATUS_BAD_SCALE 8      /* fp8 cache: a row scale outside 2^-117 .. 2^119 powers of two */
 
 /*
  * Number of workgroups to plan for on `device`: its compute-unit count.
@@ -201,17 +202,21 @@ int mla_decode_sparse_fwd(const void* q, const void* kv_cache, int64_t num_block
  *           bytes 512..639  the 64 rope values as bf16,
  *           bytes 640..643  the row's fp32 scale (latent value = code value * scale),
  *           bytes 644..655  padding.
- * The scale must be a positive normal power of two (2^-126 .. 2^127), as in the OCP
- * microscaling formats' shared scales: the hardware conversion applies only its exponent
- * field, so any other value gives an unspecified result (it is not checked).  With such
- * a scale every latent value is exact in bf16.
+ * The scale must be a power of two 2^k with -117 <= k <= 119, as in the OCP
+ * microscaling formats' shared scales (a power-of-two scale is applied exactly by the
+ * hardware conversion, and in this range every code value times the scale is a normal
+ * bf16 number or zero, so every latent value is exact in bf16).  The main kernel checks
+ * the scale of every row it reads (the rows [0, L_b) of each sequence): a row with any
+ * other scale (not a power of two, outside the range, negative, zero, NaN) sets
+ * MLA_STATUS_BAD_SCALE and makes that sequence's out and lse NaN.
  * Everything else as mla_decode_fwd with dtype bf16 (q bf16, out/lse fp32, the same
  * definition over the dequantized rows).  One call enqueues the split scheduler (it
  * writes `meta`), the main kernel, which copies each 656-byte-row page into LDS and
  * widens it there to bf16 before the page's products, and the combine.  meta/workspace:
  * device buffers of at least the sizes mla_fp8_plan_size returns (the same as
  * mla_plan_size's).  Errors and status bits as for mla_decode_fwd (a block number
- * outside the pool: MLA_STATUS_BAD_BLOCK and NaN for that sequence).
+ * outside the pool: MLA_STATUS_BAD_BLOCK and NaN for that sequence; a row scale outside
+ * the format: MLA_STATUS_BAD_SCALE and NaN for that sequence).
  */
 int mla_fp8_plan_size(int batch, int s_q, int num_heads, int max_blocks_per_seq,
                       int num_workgroups, size_t* meta_bytes, size_t* workspace_bytes);

@@ -26,6 +26,7 @@ MLA_DTYPE_BF16 = 1
 MLA_STATUS_BAD_SEQLEN = 1
 MLA_STATUS_BAD_BLOCK = 2
 MLA_STATUS_PLAN_MISMATCH = 4
+MLA_STATUS_BAD_SCALE = 8
 PAGE = 64
 D_QK = 576
 D_V = 512

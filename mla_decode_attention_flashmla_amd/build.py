@@ -15,6 +15,10 @@ LIB = os.path.join(PKG, "libmla_decode.so")
 SOURCES = ["mla_abi.hip", "mla_sched.hip", "mla_main_bf16.hip", "mla_main_f32.hip",
            "mla_combine.hip", "mla_sparse.hip", "mla_append.hip"]
 ARCH = "gfx950"
+# read-bandwidth probes for the roofline measurement (bench.py --hbm-ceiling), a library of
+# their own: nothing on the decode path links them
+PROBE_SOURCES = ["hbm_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libmla_probe.so")
 
 
 def hipcc() -> str:
@@ -39,24 +43,36 @@ def compile_flags() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libmla_decode.so in the package directory."""
-    objs = []
+    """Compile every HIP source (in parallel) and link libmla_decode.so in the package
+    directory."""
+    from concurrent.futures import ThreadPoolExecutor
+
     build_dir = os.path.join(ROOT, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    for src in SOURCES:
+    cmds, objs = [], []
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *compile_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
-               "-o", obj]
+        cmds.append([hipcc(), *compile_flags(), *EXTRA.get(src, []), "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+
+    def compile_one(cmd):
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.PIPE)
-        objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.PIPE)
-    os.replace(tmp, LIB)
+
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as pool:
+        for f in [pool.submit(compile_one, c) for c in cmds]:
+            f.result()
+    nmain = len(SOURCES)
+    for lib, lib_objs in ((LIB, objs[:nmain]), (PROBE_LIB, objs[nmain:])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.PIPE)
+        os.replace(tmp, lib)
     return LIB
 
 

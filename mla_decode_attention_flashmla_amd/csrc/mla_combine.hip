@@ -24,7 +24,8 @@ constexpr int kBatch = 4;         // parts whose O loads are in flight together
 // folded here into the part's weight; otherwise fp32.
 template <bool kHalf>
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
-    int batch, int s_q, int heads, int nwg, float* __restrict__ out, float* __restrict__ lse_out,
+    int batch, int s_q, int heads, int causal, int max_blocks, int nwg, float* __restrict__ out,
+    float* __restrict__ lse_out,
     const int32_t* __restrict__ meta, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, const float* __restrict__ part_scale) {
   __shared__ float w_s[kRowsPerBlock][kMaxSplitsLds];
@@ -35,17 +36,16 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   // for these sizes, and nothing read from it is used before the header check.
   const int32_t* sr = meta + kHdrWords + (size_t)kWgWords * nwg + (size_t)seg * kSegWords;
   const int h_magic = meta[H_MAGIC], h_batch = meta[H_BATCH], h_sq = meta[H_SQ];
-  const int h_heads = meta[H_HEADS], h_nwg = meta[H_NUM_WG], groups = meta[H_NUM_GROUPS];
+  const int h_heads = meta[H_HEADS], h_nwg = meta[H_NUM_WG], h_groups = meta[H_NUM_GROUPS];
+  const int h_causal = meta[H_CAUSAL], h_maxb = meta[H_MAX_BLOCKS];
   const int nsplit = sr[S_NSPLIT], s_len = sr[S_SEQLEN], s_slot = sr[S_SLOT];
   // all of them loaded here, before the first test (kept from being sunk past it)
   asm volatile("" ::"s"(h_magic), "s"(h_batch), "s"(h_sq), "s"(h_heads), "s"(h_nwg),
-               "s"(groups), "s"(nsplit), "s"(s_len), "s"(s_slot));
-  // a plan for other sizes was already flagged by the main kernel; touch nothing
-  const bool plan_ok = (h_magic == kMagic) & (h_batch == batch) & (h_sq == s_q) &
-                       (h_heads == heads) & (h_nwg == nwg);
-  if (!plan_ok) return;
-  if (nsplit == 1) return;
+               "s"(h_groups), "s"(h_causal), "s"(h_maxb), "s"(nsplit), "s"(s_len),
+               "s"(s_slot));
+  // the row this thread writes, from the call's own sizes (the grid covers every row)
   const int M = s_q * heads;
+  const int groups = (M + kGroupRows - 1) / kGroupRows;
   const int b = seg / groups, rg = seg - b * groups;
   const int rows_in_group = min(kGroupRows, M - rg * kGroupRows);
   const int rl = threadIdx.x >> 6;            // row within this block
@@ -55,6 +55,22 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   const int row = rg * kGroupRows + row_in_group;
   const int t = row / heads, hd = row - t * heads;
   const size_t ri = ((size_t)b * s_q + t) * heads + hd;
+  // A plan made for another call (other sizes, causal flag or table width) was flagged
+  // by the main kernel, which then wrote nothing: every row of the output becomes NaN,
+  // whether its segment was split or not.
+  const bool plan_ok = (h_magic == kMagic) & (h_batch == batch) & (h_sq == s_q) &
+                       (h_heads == heads) & (h_nwg == nwg) & (h_groups == groups) &
+                       (h_causal == causal) & (h_maxb == max_blocks);
+  if (!plan_ok) {
+    if (!row_ok) return;
+    const float nan = __builtin_nanf("");
+    float4* o = (float4*)(out + ri * kDv) + 2 * lane;
+    o[0] = make_float4(nan, nan, nan, nan);
+    o[1] = make_float4(nan, nan, nan, nan);
+    if (lane == 0) lse_out[ri] = nan;
+    return;
+  }
+  if (nsplit == 1) return;
 
   if (nsplit == 0) {
     if (!row_ok) return;
@@ -170,12 +186,12 @@ hipError_t launch_combine(const Problem& p, hipStream_t stream) {
   dim3 grid(nseg, kGroupRows / kRowsPerBlock);
   if (p.part_half)
     hipLaunchKernelGGL(mla_combine_kernel<true>, grid, dim3(kThreads), 0, stream, p.batch, p.s_q,
-                       p.heads, p.num_wg, p.out, p.lse, p.meta, p.part_o, p.part_lse,
-                       p.part_scale);
+                       p.heads, p.causal, p.max_blocks, p.num_wg, p.out, p.lse, p.meta,
+                       p.part_o, p.part_lse, p.part_scale);
   else
     hipLaunchKernelGGL(mla_combine_kernel<false>, grid, dim3(kThreads), 0, stream, p.batch,
-                       p.s_q, p.heads, p.num_wg, p.out, p.lse, p.meta, p.part_o, p.part_lse,
-                       p.part_scale);
+                       p.s_q, p.heads, p.causal, p.max_blocks, p.num_wg, p.out, p.lse, p.meta,
+                       p.part_o, p.part_lse, p.part_scale);
   return hipGetLastError();
 }
 

@@ -33,8 +33,11 @@ enum Hdr {
 // the slot has no work.
 enum Wg { W_SEG_BEGIN = 0, W_BLK_BEGIN, W_SEG_END, W_BLK_END, W_FIRST_SPLIT, W_NBLK0, W_SEQLEN0 };
 // segment row: blocks, validated length (-1: invalid), block offset in the stream,
-// number of parts (0: no keys or invalid, 1: computed whole), first partial slot.
-enum Seg { S_NBLK = 0, S_SEQLEN, S_CUM, S_NSPLIT, S_SLOT, S_FIRST_ITEM };
+// number of parts (0: no keys or invalid, 1: computed whole), first partial slot, first
+// work item (-1 for a segment with no blocks), and the scheduler's own running item
+// count of a segment-aligned plan (non-decreasing over segments, empty ones included:
+// the column the work-table rows search; batches beyond its LDS arrays keep it here).
+enum Seg { S_NBLK = 0, S_SEQLEN, S_CUM, S_NSPLIT, S_SLOT, S_FIRST_ITEM, S_AL_ITEM };
 
 inline int num_groups(int s_q, int heads) { return (s_q * heads + kGroupRows - 1) / kGroupRows; }
 

@@ -361,8 +361,11 @@ __device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr
 // conflicts).  Every pair's codes and scale are read before any lane writes, so row
 // 2p's bf16 may overwrite the pair's codes and the reads are not serialized behind the
 // writes.  A wave touches only the rows and the scale area its own copies filled.  The
-// hardware conversion applies the row's scale, a power of two, exactly.
-__device__ __forceinline__ void fp8_convert(uint32_t page_lds, uint32_t scale_lds, int wave,
+// hardware conversion applies the row's scale exactly when it is a power of two 2^k with
+// -117 <= k <= 119: then every code value times the scale is a normal bf16 number (or
+// zero).  Returns true in a lane that met a scale outside that set (the row is then not
+// in the format: the caller flags the segment and makes its result NaN).
+__device__ __forceinline__ bool fp8_convert(uint32_t page_lds, uint32_t scale_lds, int wave,
                                             int lane) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -398,6 +401,14 @@ __device__ __forceinline__ void fp8_convert(uint32_t page_lds, uint32_t scale_ld
     *(lds_u32x4*)(uintptr_t)dst = widen8(lo[i], sc[i]);
     *(lds_u32x4*)(uintptr_t)(dst + 512) = widen8(hi[i], sc[i]);
   }
+  // sign 0, mantissa 0, biased exponent 10..246 (2^-117 .. 2^119)
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t bits = __float_as_uint(sc[i]);
+    bad = bad || (bits & 0x807fffffu) != 0 || (bits >> 23) - 10u > 236u;
+  }
+  return bad;
 }
 
 template <bool kGather, bool kFp8>
@@ -410,6 +421,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     float* __restrict__ part_lse, float* __restrict__ part_scale) {
   // two page buffers; fp8 pages add 1 KiB of row scales
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + (kFp8 ? 1024 : 0)];
+  // fp8 pages: the last segment in which some wave met a row scale outside the format,
+  // one slot per segment parity (a wave may start the next segment's first page while
+  // another still reads the flag of the previous segment in its epilogue)
+  __shared__ int bad_scale_seg[2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;     // which half of the wave (token/column sub-block)
@@ -552,6 +567,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   // the softmax, where no LDS read waits behind the scalar load)
   int pre_id = 0, pre_blk = -1;
 
+  if constexpr (kFp8) {
+    // cleared before any wave can flag its first page
+    if (threadIdx.x < 2) bad_scale_seg[threadIdx.x] = -1;
+    __syncthreads();
+  }
   int seg = seg_first;
   int blk = blk_first;
   int buf = 0;
@@ -630,8 +650,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       wait_dma();
       if constexpr (kFp8) {
         // each wave widens the rows its own copies filled (no barrier needed before), and
-        // the barrier after it publishes the page and ends every wave's previous page
-        fp8_convert(lds0 + buf * kBufBytes, scale_lds, wave, lane);
+        // the barrier after it publishes the page (and any bad-scale flag) and ends every
+        // wave's previous page
+        if (__builtin_amdgcn_ballot_w64(fp8_convert(lds0 + buf * kBufBytes, scale_lds, wave,
+                                                    lane)) != 0) {
+          if (lane == 0) bad_scale_seg[seg & 1] = seg;
+        }
       }
       __syncthreads();
       PageSrc nps;
@@ -829,7 +853,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     // ---- epilogue: this segment's rows, whole or as one part ----
     // wait states for the last PV MFMA's O^T before it is read
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    const bool bad = bad_block || mismatch;
+    bool bad_scale = false;
+    if constexpr (kFp8) bad_scale = bad_scale_seg[seg & 1] == seg;
+    const bool bad = bad_block || mismatch || bad_scale;
     if (wave_active) {
       const int nsplit = seg_nsplit;
       const bool whole = nsplit == 1;
@@ -903,7 +929,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     }
     if (bad && threadIdx.x == 0)
       atomicOr(&meta[H_STATUS], (bad_block ? MLA_STATUS_BAD_BLOCK : 0) |
-                                    (mismatch ? MLA_STATUS_PLAN_MISMATCH : 0));
+                                    (mismatch ? MLA_STATUS_PLAN_MISMATCH : 0) |
+                                    (bad_scale ? MLA_STATUS_BAD_SCALE : 0));
 
     // next segment with blocks
     int nseg = seg + 1;

@@ -120,9 +120,12 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
   int32_t* seg = wg + (size_t)kWgWords * num_wg;
   auto NB = [&](int s) -> int32_t& { return in_lds ? l_nblk[s] : seg[(size_t)s * kSegWords + S_NBLK]; };
   auto CUM = [&](int s) -> int32_t& { return in_lds ? l_cum[s] : seg[(size_t)s * kSegWords + S_CUM]; };
-  // first item of a segment (segment-aligned plans)
+  // first item of a segment (segment-aligned plans), defined for every segment: an empty
+  // one holds the next segment's, so the column never decreases.  Outside LDS it has a
+  // word of its own: S_FIRST_ITEM is rewritten with -1 for empty segments in step 6,
+  // while step 7 still searches this column.
   auto ITEM = [&](int s) -> int32_t& {
-    return in_lds ? l_item[s] : seg[(size_t)s * kSegWords + S_FIRST_ITEM];
+    return in_lds ? l_item[s] : seg[(size_t)s * kSegWords + S_AL_ITEM];
   };
 
   __shared__ int64_t sh_plan[4];  // T, n, c_al, slots when one wave plans the segments

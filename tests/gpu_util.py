@@ -67,3 +67,29 @@ def check(out, lse, ref_o, ref_l, dtype, batches=None, what=""):
     assert e_o <= rel, f"{what}: O error {e_o:.3e} > {rel}"
     assert e_l <= ab, f"{what}: LSE error {e_l:.3e} > {ab}"
     return e_o, e_l
+
+
+def check_every_sequence(out, lse, oracle_one, batch, dtype, what=""):
+    """Compare every sequence of a workload with the oracle, element by element, at the
+    stated tolerances: the oracle runs one sequence at a time (oracle_one(b) returns that
+    sequence's O [s_q, H, 512] and LSE [s_q, H] in float64), so memory stays flat at any
+    batch.  The error norm is the workload's: max|O - O_ref| over all sequences divided by
+    max|O_ref| over all sequences; max|LSE - LSE_ref| absolute."""
+    rel, ab = TOL[dtype]
+    d_o = ref_max = d_l = 0.0
+    for b in range(batch):
+        ro, rl = oracle_one(b)
+        o, l = out[b], lse[b]
+        assert np.isfinite(o).all(), f"{what}: non-finite O in sequence {b}"
+        assert np.array_equal(np.isneginf(rl), np.isneginf(l)), f"{what}: -inf LSE pattern, sequence {b}"
+        d_o = max(d_o, float(np.abs(o - ro).max()))
+        ref_max = max(ref_max, float(np.abs(ro).max()))
+        fin = np.isfinite(rl)
+        if fin.any():
+            d_l = max(d_l, float(np.abs(l[fin] - rl[fin]).max()))
+    e_o = d_o / max(ref_max, 1e-30)
+    announce(f"{what}: all {batch} sequences: max|dO|/max|O| = {e_o:.3e} (tol {rel}), "
+             f"max|dLSE| = {d_l:.3e} (tol {ab})")
+    assert e_o <= rel, f"{what}: O error {e_o:.3e} > {rel}"
+    assert d_l <= ab, f"{what}: LSE error {d_l:.3e} > {ab}"
+    return e_o, d_l

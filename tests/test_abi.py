@@ -13,6 +13,14 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "mla_decode.h")
 
 
+# These tests hand made-up device addresses to the compute entry points: a clean error
+# code proves validation ran before any HIP call.  Where a GPU is visible, a validation
+# regression would launch kernels on those addresses, so they run only without one.
+GPU_VISIBLE = os.path.exists("/dev/kfd")
+fake_pointers = pytest.mark.skipif(GPU_VISIBLE, reason="passes fake device pointers; "
+                                   "runs only where no GPU is visible")
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(B.LIB_PATH):
@@ -68,6 +76,7 @@ def _fwd(lib, **kw):
                               a["ws"], a["ws_bytes"], a["stream"])
 
 
+@fake_pointers
 def test_decode_rejects_bad_arguments_without_touching_hip(lib):
     # the pointers are fake: any call that got past validation would fail or fault,
     # so a clean error code proves validation ran first
@@ -94,6 +103,7 @@ def test_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _fwd(lib, batch=0, q=None, out=None) == B.MLA_OK
 
 
+@fake_pointers
 def test_metadata_rejects_bad_arguments(lib):
     f = lib.mla_get_split_metadata
     assert f(None, 2, 1, 16, 0, 4, 8, 0, 4096, 1 << 20, None) == B.MLA_ERR_INVALID_ARG
@@ -104,6 +114,7 @@ def test_metadata_rejects_bad_arguments(lib):
     assert f(4096, 2, 1, 16, 0, 4, 8, -3, 8192, 1 << 20, None) == B.MLA_ERR_INVALID_ARG
 
 
+@fake_pointers
 def test_status_read_rejects_null(lib):
     v = ctypes.c_int32(0)
     assert lib.mla_read_status(None, None, ctypes.byref(v)) == B.MLA_ERR_INVALID_ARG
@@ -135,6 +146,7 @@ def _sparse(lib, **kw):
                                      a["ws"], a["ws_bytes"], a["stream"])
 
 
+@fake_pointers
 def test_sparse_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _sparse(lib, topk=100) == B.MLA_ERR_INVALID_ARG       # not a multiple of 64
     assert _sparse(lib, topk=0) == B.MLA_ERR_INVALID_ARG
@@ -160,6 +172,7 @@ def _fp8(lib, **kw):
                                   a["ws"], a["ws_bytes"], a["stream"])
 
 
+@fake_pointers
 def test_fp8_decode_rejects_bad_arguments_without_touching_hip(lib):
     # the fp8 rows are widened inside the main kernel: the same plan as bf16 decode
     assert B.fp8_plan_size(2, 1, 128, 10, 256) == B.plan_size(2, 1, 128, 256)
@@ -172,3 +185,29 @@ def test_fp8_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _fp8(lib, meta_bytes=16) == B.MLA_ERR_PLAN
     assert _fp8(lib, ws_bytes=1024) == B.MLA_ERR_PLAN
     assert _fp8(lib, batch=0, q=None, out=None) == B.MLA_OK
+
+
+def test_strided_tensors_are_rejected_on_the_host():
+    """The boundary takes dense row-major buffers only (plain pointers, no strides): the
+    binding refuses a strided view, e.g. q sliced out of a wider projection output or a
+    transposed out, before any library call, so a caller must copy it first."""
+    import torch
+
+    qw = torch.zeros((2, 1, 16, 640), dtype=torch.bfloat16)
+    q = qw[..., :576]                                     # rows 640 elements apart
+    kv = torch.zeros((4, 64, 576), dtype=torch.bfloat16)
+    table = torch.zeros((2, 2), dtype=torch.int32)
+    lens = torch.zeros(2, dtype=torch.int32)
+    out = torch.zeros((2, 1, 16, 512))
+    lse = torch.zeros((2, 1, 16))
+    plan = B.Plan(torch.zeros(16, dtype=torch.int32), torch.zeros(16, dtype=torch.uint8),
+                  2, 1, 16, 0, 2, 8)
+    assert not q.is_contiguous()
+    with pytest.raises(ValueError, match="contiguous"):
+        B.decode_fwd(q, kv, table, lens, 0.1, out, lse, plan)
+    out_t = torch.zeros((2, 1, 512, 16)).transpose(2, 3)
+    with pytest.raises(ValueError, match="contiguous"):
+        B.decode_fwd(q.contiguous(), kv, table, lens, 0.1, out_t, lse, plan)
+    with pytest.raises(ValueError, match="contiguous"):
+        B.decode_fp8_fwd(q, torch.zeros((4, 64, 656), dtype=torch.uint8), table, lens, 0.1,
+                         out, lse, plan)

@@ -5,8 +5,8 @@ row's fp32 scale, a power of two.  The oracle dequantizes exactly (fp64); the GP
 widens each page to bf16 in LDS, which is exact for such scales, and decodes in bf16,
 so the bar is the bf16 tolerance.  Covered: ragged lengths around block boundaries,
 causal multi-token queries and 16-token chunks, several row groups, forced splits, a block number outside
-the pool (status bit, NaN for that sequence only), the full 64 x 8K workload on sampled
-sequences, and bit-for-bit agreement with the bf16 path over a cache that holds the
+the pool and row scales outside the format (status bits, NaN for that sequence only),
+every sequence of the full 64 x 8K workload, and bit-for-bit agreement with the bf16 path over a cache that holds the
 dequantized rows.
 """
 
@@ -20,7 +20,7 @@ from mla_decode_attention_flashmla_amd import binding as B
 from mla_decode_attention_flashmla_amd import inputs as I
 from oracle import mla_oracle as O
 
-from gpu_util import announce, check, run
+from gpu_util import announce, check, check_every_sequence, run
 
 pytestmark = pytest.mark.gpu
 
@@ -86,14 +86,45 @@ def test_fp8_bad_block_flags_only_its_sequence():
 
 
 def test_fp8_full_size_workload():
+    """Every sequence of the 64 x 8K fp8 workload against the oracle."""
     w = I.FP8_WORKLOADS["fp8_b64_l8192"]
     d = full_workload()
-    batches = I.sample_sequences(w.batch, 6, w.seed)
-    announce(f"fp8 full size, sampled sequences {batches.tolist()}")
+    announce("fp8 full size")
     out, lse, status = run_fp8(d)
     assert status == 0 and np.isfinite(out).all() and np.isfinite(lse).all()
-    ref_o, ref_l = oracle(d, batches=batches)
-    check(out, lse, ref_o, ref_l, "bf16", batches=batches, what="fp8 full size")
+
+    def one(b):
+        o, l = O.mla_decode_fp8(d["q"][b:b + 1], d["kv_cache"], d["block_table"][b:b + 1],
+                                d["seqlens"][b:b + 1], d["scale"], d["causal"])
+        return o[0], l[0]
+    check_every_sequence(out, lse, one, w.batch, "bf16", what="fp8 full size")
+
+
+# row scales outside the format: not a power of two, below 2^-117, above 2^119, negative,
+# zero, NaN
+BAD_SCALES = [0.75, 2.0 ** -118, 2.0 ** 120, -2.0 ** -8, 0.0, float("nan")]
+
+
+@pytest.mark.parametrize("bad", BAD_SCALES)
+@pytest.mark.parametrize("nwg", [None, 9])
+def test_fp8_row_scale_outside_the_format(bad, nwg):
+    """A row whose scale is not in the format (the oracle rejects such a sequence) sets
+    MLA_STATUS_BAD_SCALE and makes that sequence's O and LSE NaN, split or not; the
+    other sequences, and a bad scale in a row past a sequence's length, are unaffected."""
+    w = I.Workload("fp8scale", 3, 1, 128, 700, "bf16", 192, ragged=True, seed=72)
+    d = I.make_fp8_workload(w, seqlens=[700, 300, 130])
+    kv = d["kv_cache"]
+    # sequence 1, row 200 (page 3); sequence 2, row 140 (past its length 130, page 2)
+    kv[d["block_table"][1, 3], 200 - 192, 640:644] = np.array([bad], np.float32).view(np.uint8)
+    kv[d["block_table"][2, 2], 140 - 128, 640:644] = np.array([bad], np.float32).view(np.uint8)
+    with pytest.raises(ValueError):
+        oracle(d, batches=[1])
+    announce(f"fp8 bad row scale {bad!r}, nwg={nwg}")
+    out, lse, status = run_fp8(d, nwg)
+    assert status == B.MLA_STATUS_BAD_SCALE
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    ref_o, ref_l = oracle(d, batches=[0, 2])
+    check(out, lse, ref_o, ref_l, "bf16", batches=[0, 2], what="fp8 sequences without it")
 
 
 def exact_bf16_cache(kv_fp8, chunk=256):

@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Small cases are compared element by element in full; the full-size workloads in
-the launch configuration the bench times are compared on whole sampled
-sequences (every head, every key), the oracle computing those one by one.
+Every case is compared element by element in full, the full-size workloads too (in
+the launch configuration the bench times): the oracle computes their sequences one
+by one.
 """
 
 import numpy as np
@@ -13,7 +13,7 @@ from mla_decode_attention_flashmla_amd import binding as B
 from mla_decode_attention_flashmla_amd import inputs as I
 from oracle import mla_oracle as O
 
-from gpu_util import announce, check, run, to_device
+from gpu_util import announce, check, check_every_sequence, run, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -225,6 +225,57 @@ def test_stale_plan_is_flagged():
     assert np.isnan(out[1].cpu().numpy()).all() and np.isnan(lse[1].cpu().numpy()).all()
 
 
+def check_plan(m, nwg, nb, minb):
+    """Invariants of a split plan (metadata words m) for block counts nb per segment:
+    every block of every segment is covered by exactly one workgroup range, the item
+    count and sizes follow the documented rule, part counts and partial slots agree."""
+    nseg = int(m[7])
+    wg = m[32:32 + 8 * nwg].reshape(nwg, 8)
+    seg = m[32 + 8 * nwg:32 + 8 * nwg + 8 * nseg].reshape(nseg, 8)
+    assert nseg == len(nb) and m[6] == 0
+    T, n, c_al = int(m[9]), int(m[10]), int(m[13])
+    assert np.array_equal(seg[:, 0], nb) and T == int(nb.sum())
+    c_min = -(-T // nwg)
+    if minb == 0 and c_al > 0:
+        # segment-aligned: the smallest item size >= c_min whose items fit one per
+        # workgroup, at most 4 blocks above c_min
+        assert c_min <= c_al <= c_min + 4
+        assert n == int((-(-nb // c_al)).sum()) <= nwg
+        assert c_al == c_min or int((-(-nb // (c_al - 1))).sum()) > nwg
+    elif minb == 0:
+        # stream cut: the fewest items whose largest is as short as with one per slot
+        assert n == -(-T // c_min), (T, nwg, n)
+    else:
+        assert n == min(max(T // minb, 1), nwg, T)
+    cover = [np.zeros(k, int) for k in seg[:, 0]]
+    parts = np.zeros(nseg, int)
+    longest = 0
+    for r in wg:
+        if r[0] < 0:
+            continue
+        size = 0
+        for s in range(r[0], r[2] + 1):
+            b0 = r[1] if s == r[0] else 0
+            b1 = r[3] if s == r[2] else seg[s, 0]
+            if b1 > b0:
+                cover[s][b0:b1] += 1
+                parts[s] += 1
+                size += b1 - b0
+        longest = max(longest, size)
+    if minb == 0 and c_al > 0:
+        assert longest <= c_al
+        assert all(r[0] == r[2] for r in wg if r[0] >= 0)    # no range crosses segments
+    else:
+        assert longest == -(-T // n)
+    assert all((c == 1).all() for c in cover)
+    assert np.array_equal(parts, seg[:, 3])
+    multi = seg[:, 3] > 1
+    slots = np.concatenate([np.arange(a, a + k) for a, k in zip(seg[multi, 4], seg[multi, 3])]) \
+        if multi.any() else np.zeros(0)
+    assert len(set(slots.tolist())) == len(slots) and (slots < nwg + nseg).all()
+    return c_al
+
+
 # (sequences, query tokens): 74 segments (the scheduler's block-wide path), exactly 64
 # and 33 (its one-wave path)
 @pytest.mark.parametrize("batch,s_q", [(37, 2), (32, 2), (33, 1)])
@@ -237,79 +288,100 @@ def test_scheduler_partition_invariants(batch, s_q):
     d = I.make_workload(w)
     d["seqlens"][5] = 2
     t = to_device(d)
+    nb = np.repeat((d["seqlens"] + 63) // 64, groups)
     for nwg, minb in ((256, 0), (256, 1), (13, 3), (1000, 1), (1000, 0), (7, 0), (60, 0),
                       (100, 0)):
         announce(f"scheduler batch={batch} s_q={s_q} nwg={nwg} min_split={minb}")
         plan = B.alloc_plan(batch, s_q, 128, s_q > 1, t["table"].shape[1], nwg)
         B.get_split_metadata(t["lens"], plan, minb)
         torch.cuda.synchronize()
-        m = plan.meta.cpu().numpy()
-        nseg = m[7]
-        wg = m[32:32 + 8 * nwg].reshape(nwg, 8)
-        seg = m[32 + 8 * nwg:32 + 8 * nwg + 8 * nseg].reshape(nseg, 8)
-        assert nseg == batch * groups and m[6] == 0
-        T, n, c_al = int(m[9]), int(m[10]), int(m[13])
-        lens = d["seqlens"]
-        nb = np.repeat((lens + 63) // 64, groups)
-        assert np.array_equal(seg[:, 0], nb)
-        c_min = -(-T // nwg)
-        if minb == 0 and c_al > 0:
-            # segment-aligned: the smallest item size >= c_min whose items fit one per
-            # workgroup, at most 4 blocks above c_min
-            assert c_min <= c_al <= c_min + 4
-            assert n == int((-(-nb // c_al)).sum()) <= nwg
-            assert c_al == c_min or int((-(-nb // (c_al - 1))).sum()) > nwg
-        elif minb == 0:
-            # stream cut: the fewest items whose largest is as short as with one per slot
-            assert n == -(-T // c_min), (T, nwg, n)
-        else:
-            assert n == min(max(T // minb, 1), nwg, T)
-        cover = [np.zeros(n, int) for n in seg[:, 0]]
-        parts = np.zeros(nseg, int)
-        longest = 0
-        for r in wg:
-            if r[0] < 0:
-                continue
-            size = 0
-            for s in range(r[0], r[2] + 1):
-                b0 = r[1] if s == r[0] else 0
-                b1 = r[3] if s == r[2] else seg[s, 0]
-                if b1 > b0:
-                    cover[s][b0:b1] += 1
-                    parts[s] += 1
-                    size += b1 - b0
-            longest = max(longest, size)
-        if minb == 0 and c_al > 0:
-            assert longest <= c_al
-            assert all(r[0] == r[2] for r in wg if r[0] >= 0)    # no range crosses segments
-        else:
-            assert longest == -(-T // n)
-        assert all((c == 1).all() for c in cover)
-        assert np.array_equal(parts, seg[:, 3])
-        multi = seg[:, 3] > 1
-        slots = np.concatenate([np.arange(s, s + n) for s, n in zip(seg[multi, 4], seg[multi, 3])]) \
-            if multi.any() else np.zeros(0)
-        assert len(set(slots.tolist())) == len(slots) and (slots < nwg + nseg).all()
+        check_plan(plan.meta.cpu().numpy(), nwg, nb, minb)
+
+
+def test_scheduler_beyond_lds_segments():
+    """More segments than the scheduler keeps in LDS (its per-segment arrays then live in
+    the metadata buffer): 5000 sequences, 200 of them 1024 tokens long and the rest
+    empty, so the segment-aligned plan (16-block items) is taken and its item column has
+    runs of empty segments.  The plan's invariants hold, and every sequence matches the
+    oracle (empty ones: O = 0, LSE = -inf)."""
+    batch, heads = 5000, 16
+    lens = np.zeros(batch, np.int32)
+    rng = np.random.default_rng(44)
+    lens[np.sort(rng.choice(batch, 200, replace=False))] = 1024
+    lens[-1] = 0
+    w = I.Workload("manyseg", batch, 1, heads, 1024, "bf16", 192, ragged=True, seed=44)
+    d = I.make_workload(w, seqlens=lens)
+    t = to_device(d)
+    nwg = 256
+    nb = (lens + 63) // 64
+    for minb in (0, 1):
+        announce(f"scheduler with {batch} segments, min_split={minb}")
+        plan = B.alloc_plan(batch, 1, heads, False, t["table"].shape[1], nwg)
+        B.get_split_metadata(t["lens"], plan, minb)
+        torch.cuda.synchronize()
+        c_al = check_plan(plan.meta.cpu().numpy(), nwg, nb, minb)
+        if minb == 0:
+            assert c_al == 16
+        out, lse, st, _ = run(d, t, plan=plan)
+        assert st == 0
+        check_every_sequence(out, lse, oracle_one(d), batch, "bf16",
+                             what=f"{batch} segments, min_split={minb}")
+
+
+def test_plan_for_another_table_width_or_mask_gives_nan():
+    """A plan built for another table width or causal flag is flagged, and every output
+    row becomes NaN (split segments and whole ones alike)."""
+    import dataclasses
+
+    w = I.Workload("width", 3, 2, 128, 600, "bf16", 192, causal=True, ragged=True, seed=45)
+    d = I.make_workload(w, seqlens=[600, 70, 200])
+    t = to_device(d)
+    announce("plan for another table width / causal flag")
+    _, _, st, plan = run(d, t, num_workgroups=16, min_split_blocks=2)
+    assert st == 0
+    wide = torch.full((3, t["table"].shape[1] + 3), -1, dtype=torch.int32, device="cuda")
+    wide[:, :t["table"].shape[1]] = t["table"]
+    cases = [("table width", dict(t, table=wide), plan),
+             ("causal flag", t, dataclasses.replace(plan, causal=0))]
+    for what, tt, pl in cases:
+        B.get_split_metadata(t["lens"], plan)          # a fresh plan, clean status
+        out = torch.zeros((3, 2, 128, 512), device="cuda")
+        lse = torch.zeros((3, 2, 128), device="cuda")
+        B.decode_fwd(tt["q"], tt["kv"], tt["table"], tt["lens"], float(d["scale"]), out, lse, pl)
+        assert B.read_status(plan) & B.MLA_STATUS_PLAN_MISMATCH, what
+        assert torch.isnan(out).all().item() and torch.isnan(lse).all().item(), what
 
 
 # ---------------------------------------------------------------- full-size workloads
 
-FULL = [("paged_b16_l4096", 16), ("ragged_b64_l8192", 8), ("gate_b64_l8192", 6),
-        ("spec_b128_sq2_l16384", 4), ("long_b4_l131072", 2)]
+FULL = ["tiny_fp32_dense", "paged_b16_l4096", "ragged_b64_l8192", "gate_b64_l8192",
+        "spec_b128_sq2_l16384", "long_b4_l131072"]
 
 
-@pytest.mark.parametrize("name,nsample", FULL)
-def test_full_size_workload(name, nsample):
+def oracle_one(d):
+    """The oracle on sequence b alone (its own slices of q, table and lengths)."""
+    w = d["workload"]
+
+    def one(b):
+        o, l = O.mla_decode(d["q"][b:b + 1], d["kv_cache"], d["block_table"][b:b + 1],
+                            d["seqlens"][b:b + 1], d["scale"], d["causal"], dtype=w.dtype)
+        return o[0], l[0]
+    return one
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    """Every sequence of every full-size workload, in the bench's launch configuration
+    (the device's workgroup count, the default plan)."""
     w = I.WORKLOADS[name]
     announce(f"full-size {name}: generating")
     d = I.make_workload(w)
-    batches = I.sample_sequences(w.batch, nsample, w.seed)
-    announce(f"full-size {name}: GPU run, sampled sequences {batches.tolist()}")
+    announce(f"full-size {name}: GPU run")
     out, lse, st, _ = run(d)
     assert st == 0
     assert np.isfinite(out).all() and np.isfinite(lse).all()
-    ref_o, ref_l = oracle(d, batches=batches)
-    check(out, lse, ref_o, ref_l, w.dtype, batches=batches, what=name)
+    announce(f"full-size {name}: oracle, {w.batch} sequences")
+    check_every_sequence(out, lse, oracle_one(d), w.batch, w.dtype, what=name)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -355,20 +427,11 @@ def test_chunked_queries(heads, s_q, lens, dtype):
 
 
 def test_chunked_full_size_workload():
-    """64-token chunks of 4 sequences over 8K caches (the chunked bench workload), on
-    sampled query tokens of every sequence."""
+    """64-token chunks of 4 sequences over 8K caches (the chunked bench workload): every
+    query token of every sequence."""
     w = I.WORKLOADS["chunk_b4_sq64_l8192"]
     d = I.make_workload(w)
     announce("full-size chunk_b4_sq64_l8192")
     out, lse, st, _ = run(d)
     assert st == 0 and np.isfinite(out).all() and np.isfinite(lse).all()
-    tok = [0, 1, 31, 63]
-    # the oracle on the sampled tokens: token t of the chunk sees keys up to L - 64 + t
-    ref_o = np.empty((w.batch, len(tok), w.heads, 512))
-    ref_l = np.empty((w.batch, len(tok), w.heads))
-    for k, t in enumerate(tok):
-        lens_t = (d["seqlens"] - (w.s_q - 1 - t)).astype(np.int32)
-        o, l = O.mla_decode(d["q"][:, t:t + 1], d["kv_cache"], d["block_table"], lens_t,
-                            d["scale"], False)
-        ref_o[:, k], ref_l[:, k] = o[:, 0], l[:, 0]
-    check(out[:, tok], lse[:, tok], ref_o, ref_l, "bf16", what="chunk full size")
+    check_every_sequence(out, lse, oracle_one(d), w.batch, "bf16", what="chunk full size")
