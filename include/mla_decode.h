@@ -20,8 +20,10 @@
  *
  * Memory.  Every pointer argument below is a DEVICE pointer except `status`
  * (host) in mla_read_status.  The caller owns all buffers; the library never
- * allocates device memory and keeps no per-call state.  Inputs are never
- * modified.  All tensors are dense and row-major:
+ * allocates device memory and keeps no per-call state (mla_decode_fwd_noalloc
+ * keeps its plan and partials in the library's static scratch instead).  Inputs
+ * are never modified.  All tensors are dense and row-major (a strided view, e.g. q
+ * sliced from a wider projection output, must be copied to a dense buffer first):
  *
  *   q            [batch][s_q][num_heads][576]        dtype (16-byte aligned)
  *   kv_cache     [num_blocks][64][576]               dtype (16-byte aligned)
@@ -62,6 +64,7 @@ extern "C" {
 #define MLA_ERR_UNSUPPORTED (-2) /* unknown dtype, s_q * num_heads above MLA_MAX_ROWS */
 #define MLA_ERR_PLAN (-3)        /* metadata or workspace buffer too small for these sizes */
 #define MLA_ERR_HIP (-4)         /* a HIP runtime call failed (launch, copy, device query) */
+#define MLA_ERR_SCRATCH (-5)     /* mla_decode_fwd_noalloc: sizes need more than its fixed scratch */
 
 /* Element types of q and kv_cache (out/lse are always float32). */
 #define MLA_DTYPE_F32 0
@@ -250,6 +253,36 @@ int mla_decode_fp8_fwd(const void* q, const void* kv_fp8, int64_t num_blocks,
 int mla_kv_append(int dtype, const void* new_kv, void* kv_cache, int64_t num_blocks,
                   const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens,
                   int batch, int s_new, int32_t* status, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mla_get_split_metadata followed by
+ * mla_decode_fwd (the default plan, min_split_blocks = 0) in one call, with the plan
+ * and the partial results of split sequences kept in the library's own static device
+ * scratch of MLA_NOALLOC_SCRATCH_BYTES (80 MiB) per device, instead of caller buffers.
+ * The caller still passes inputs and outputs, with the meaning, layout and checks of
+ * mla_decode_fwd.  The call allocates nothing (no hipMalloc/hipFree, no allocating
+ * library routine); the scratch is part of the loaded library and each device that runs
+ * the call holds its own copy until the process ends.  Its address is looked up once
+ * per device, on the first call with that device current.
+ * Limit: the plan (32 + 8 * (num_workgroups + segments) int32, rounded up to 256 bytes)
+ * plus the partials ((num_workgroups + segments) * 128 rows of 1032 bytes for bf16, of
+ * 2052 bytes for fp32; segments = batch * ceil(s_q * num_heads / 128)) must fit the
+ * scratch, else MLA_ERR_SCRATCH and nothing is enqueued (with 256 workgroups: up to 378
+ * segments in bf16, 63 in fp32).
+ * Every call on one device shares that device's scratch: calls whose work overlaps on a
+ * device (other streams, or other threads, without ordering between them) race and give
+ * wrong results; calls ordered on one stream are safe.  The scratch keeps the last
+ * call's plan; each call rewrites every word it reads, so nothing is cleared.  Device
+ * status bits are not readable here (the plan lives in the scratch): problems only the
+ * device can see show as NaN outputs for the affected sequences, as in mla_decode_fwd.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (80u << 20)
+int mla_decode_fwd_noalloc(int dtype, const void* q, const void* kv_cache, int64_t num_blocks,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           const int32_t* seqlens, int batch, int s_q, int num_heads,
+                           int causal, float scale, float* out, float* lse,
+                           int num_workgroups, void* stream);
 
 /*
  * Synchronizes `stream`, then copies the plan's device status word

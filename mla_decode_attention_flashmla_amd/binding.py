@@ -21,6 +21,8 @@ MLA_ERR_INVALID_ARG = -1
 MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_PLAN = -3
 MLA_ERR_HIP = -4
+MLA_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 80 << 20
 MLA_DTYPE_F32 = 0
 MLA_DTYPE_BF16 = 1
 MLA_STATUS_BAD_SEQLEN = 1
@@ -34,7 +36,7 @@ D_V = 512
 EXPORTS = ("mla_device_workgroups", "mla_plan_size", "mla_get_split_metadata",
            "mla_decode_fwd", "mla_decode_main", "mla_decode_combine", "mla_sparse_plan_size",
            "mla_decode_sparse_fwd", "mla_fp8_plan_size", "mla_decode_fp8_fwd", "mla_kv_append",
-           "mla_read_status", "mla_status_string")
+           "mla_read_status", "mla_status_string", "mla_decode_fwd_noalloc")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -75,6 +77,8 @@ def load() -> ctypes.CDLL:
                                        c_int, c_f, c_p, c_p, c_p, c_sz, c_int, c_p, c_sz, c_p]
     lib.mla_kv_append.argtypes = [c_int, c_p, c_p, c_i64, c_p, c_int, c_p, c_int, c_int, c_p,
                                   c_p]
+    lib.mla_decode_fwd_noalloc.argtypes = [c_int, c_p, c_p, c_i64, c_p, c_int, c_p, c_int,
+                                           c_int, c_int, c_int, c_f, c_p, c_p, c_int, c_p]
     lib.mla_read_status.argtypes = [c_p, c_p, ctypes.POINTER(ctypes.c_int32)]
     lib.mla_status_string.argtypes = [c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -189,6 +193,30 @@ def decode_main(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream
 def decode_combine(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream=None):
     _decode("mla_decode_combine", q, kv_cache, block_table, seqlens, scale, out, lse, plan,
             stream)
+
+
+def decode_fwd_noalloc(q, kv_cache, block_table, seqlens, scale, out, lse, causal=False,
+                       num_workgroups: Optional[int] = None, stream=None) -> None:
+    """mla_decode_fwd_noalloc: plan, main kernel and combine in one call, with the plan and
+    partial results in the library's static scratch (no device allocation, no plan
+    buffers)."""
+    lib = load()
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seqlens", seqlens), ("out", out), ("lse", lse)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, s_q, H, D = q.shape
+    if (D != D_QK or kv_cache.shape[1:] != (PAGE, D_QK) or block_table.shape[0] != B
+            or tuple(out.shape) != (B, s_q, H, D_V) or tuple(lse.shape) != (B, s_q, H)
+            or kv_cache.dtype != q.dtype):
+        raise ValueError("shape/dtype mismatch with q [B,s_q,H,576], kv [n,64,576]")
+    if num_workgroups is None:
+        num_workgroups = device_workgroups(q.device.index or 0)
+    _check("mla_decode_fwd_noalloc", lib.mla_decode_fwd_noalloc(
+        _dtype_code(q), q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
+        block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), B, s_q, H,
+        int(bool(causal)), float(scale), out.data_ptr(), lse.data_ptr(), num_workgroups,
+        _stream(stream)))
 
 
 def sparse_plan_size(batch: int, heads: int, topk: int, num_workgroups: int) -> tuple[int, int]:

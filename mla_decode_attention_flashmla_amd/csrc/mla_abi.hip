@@ -1,14 +1,25 @@
 // C ABI of libmla_decode.so: host-side validation, plan sizing and launches.
 //
 // Every argument check happens before the first HIP call, so a rejected call
-// enqueues nothing and needs no GPU.  The library allocates no device memory.
+// enqueues nothing and needs no GPU.  The library allocates no device memory: callers
+// pass every buffer, except for mla_decode_fwd_noalloc, whose scratch is static device
+// data of the library.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "mla_decode.h"
 #include "mla_internal.h"
 
 using namespace mla;
+
+// Scratch of mla_decode_fwd_noalloc: the split plan, then the partial results of split
+// segments.  Each device that runs the call holds its own copy for the life of the
+// process.  In host code `scratch` names a host-side stand-in, not the device memory:
+// only the address hipGetSymbolAddress returns (kept per device below) is handed to
+// kernels.
+static __device__ __attribute__((aligned(256))) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -328,6 +339,106 @@ int mla_kv_append(int dtype, const void* new_kv, void* kv_cache, int64_t num_blo
   return MLA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept; nullptr if the lookup fails.
+char* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    p = (char*)addr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// Compact partial-result layout of the no-allocation call, for `slots` part slots:
+// fp16 O [slots][128][512], then the per-row scales and LSEs [slots][128] (bf16
+// inputs), or fp32 O then the LSEs (fp32 inputs).
+size_t noalloc_partial_bytes(bool half, size_t slots) {
+  const size_t rows = slots * kGroupRows;
+  return half ? rows * (kDv * 2 + 4 + 4) : rows * (kDv * 4 + 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_fwd_noalloc(int dtype, const void* q, const void* kv_cache, int64_t num_blocks,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           const int32_t* seqlens, int batch, int s_q, int num_heads,
+                           int causal, float scale, float* out, float* lse,
+                           int num_workgroups, void* stream) {
+  // the same host checks as mla_get_split_metadata + mla_decode_fwd, before any HIP call
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  int rc = check_sizes(batch, s_q, num_heads, num_workgroups);
+  if (rc) return rc;
+  if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (num_blocks < 0 || max_blocks_per_seq < 0) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!q || !out || !lse || !seqlens || !block_table) return MLA_ERR_INVALID_ARG;
+  if (num_blocks > 0 && !kv_cache) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (kv_cache && !aligned16(kv_cache)))
+    return MLA_ERR_INVALID_ARG;
+  const bool half = dtype == MLA_DTYPE_BF16;
+  const size_t meta_b = align256(meta_words(batch, s_q, num_heads, num_workgroups) * 4);
+  const size_t slots = num_slots(batch, s_q, num_heads, num_workgroups);
+  if (meta_b + noalloc_partial_bytes(half, slots) > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return MLA_ERR_SCRATCH;
+
+  char* base = scratch_on_current_device();
+  if (!base) return MLA_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* meta = (int32_t*)base;
+  // the scheduler writes every plan word the other kernels read (status included), and
+  // each partial is written before it is read: nothing needs clearing between calls
+  if (launch_sched(seqlens, batch, s_q, num_heads, causal, max_blocks_per_seq, num_workgroups,
+                   0, meta, st) != hipSuccess)
+    return MLA_ERR_HIP;
+  Problem p;
+  p.q = q;
+  p.kv = kv_cache;
+  p.num_blocks = num_blocks;
+  p.block_table = block_table;
+  p.max_blocks = max_blocks_per_seq;
+  p.seqlens = seqlens;
+  p.batch = batch;
+  p.s_q = s_q;
+  p.heads = num_heads;
+  p.causal = causal;
+  p.scale = scale;
+  p.out = out;
+  p.lse = lse;
+  p.meta = meta;
+  p.num_wg = num_workgroups;
+  char* part = base + meta_b;
+  const size_t rows = slots * kGroupRows;
+  p.part_o = (float*)part;
+  p.part_half = half;
+  p.part_scale = half ? (float*)(part + rows * kDv * 2) : nullptr;
+  p.part_lse = half ? (float*)(part + rows * (kDv * 2 + 4)) : (float*)(part + rows * kDv * 4);
+  p.src_row = nullptr;
+  p.fp8 = false;
+  hipError_t e = half ? launch_main_bf16(p, st) : launch_main_f32(p, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (launch_combine(p, st) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_status_string(int code) {
   switch (code) {
     case MLA_OK: return "ok";
@@ -335,6 +446,8 @@ const char* mla_status_string(int code) {
     case MLA_ERR_UNSUPPORTED: return "unsupported dtype or size";
     case MLA_ERR_PLAN: return "metadata or workspace buffer too small";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_SCRATCH: return "plan and partial results exceed the fixed scratch of the "
+                                 "no-allocation call";
     default: return "unknown status code";
   }
 }
