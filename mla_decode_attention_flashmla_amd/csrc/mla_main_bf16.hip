@@ -856,74 +856,126 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     bool bad_scale = false;
     if constexpr (kFp8) bad_scale = bad_scale_seg[seg & 1] == seg;
     const bool bad = bad_block || mismatch || bad_scale;
-    if (wave_active) {
-      const int nsplit = seg_nsplit;
-      const bool whole = nsplit == 1;
-      const float l_tot = swap_halves_sum(l_run);
-      float inv, lse_v;
-      if (bad) {
-        inv = __builtin_nanf("");
-        lse_v = __builtin_nanf("");
-      } else if (l_tot > 0.f) {
-        inv = 1.0f / l_tot;
-        lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      } else {
-        inv = 0.f;
-        lse_v = -INFINITY;
+    const bool whole = seg_nsplit == 1;
+    const float l_tot = swap_halves_sum(l_run);
+    float inv, lse_v;
+    if (bad) {
+      inv = __builtin_nanf("");
+      lse_v = __builtin_nanf("");
+    } else if (l_tot > 0.f) {
+      inv = 1.0f / l_tot;
+      lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    } else {
+      inv = 0.f;
+      lse_v = -INFINITY;
+    }
+    // One part of a split segment stores O_i in fp16 under a power-of-two scale per row
+    // that puts the row's largest |O_i| in [2^14, 2^15), so every value keeps fp16's 11
+    // significant bits and none overflows; the combine multiplies the scale back.  Half
+    // the bytes of fp32 partials, written here and read again by the combine.
+    int pe = 0;
+    float inv_s = inv;
+    if (wave_active && !whole) {
+      float amax = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < kCTiles; ++ct) {
+        float v[16];
+        o_read(ct, v);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
       }
+      amax = swap_halves_max(amax) * inv;
+      pe = __builtin_amdgcn_frexp_expf(amax);   // amax in [2^(pe-1), 2^pe)
+      pe = pe < -100 ? -100 : (pe > 100 ? 100 : pe);
+      inv_s = inv * __builtin_ldexpf(1.f, 15 - pe);
+    }
+    // The rows are written through LDS so that every store covers whole rows: in the
+    // accumulator layout a lane holds one row and a store instruction would touch 32
+    // rows with 16 bytes each.  The last page's buffer is free once every wave is done
+    // with its products (the next segment's first page, if any, is in flight into the
+    // other buffer); each wave stages its own 32 rows in a quarter of it, in passes of
+    // 512 bytes per row (256 fp16 or 128 fp32 columns).
+    __syncthreads();
+    if (wave_active) {
+      constexpr int kStagePitch = 528;   // 512 bytes + 16: rows start 4 banks apart
+      static_assert(4 * 32 * kStagePitch <= kBufBytes, "epilogue staging");
+      typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+      typedef __attribute__((address_space(3))) f16x4 lds_f16x4;
+      typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+      // lane values computed here, not hoisted to the kernel's start and kept live
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
+      const uint32_t stage = lds0 + (buf ^ 1) * kBufBytes + wave * 32 * kStagePitch;
+      const uint32_t w_off = stage + (lane_e & 31) * kStagePitch + 8 * (lane_e >> 5);
+      const int rr = lane_e >> 5, cl = lane_e & 31;              // read-back: row 2i + rr, chunk cl
+      const int row_base = rg * kGroupRows + wave * 32;          // first row of this wave
       if (whole) {
-        const size_t ri = ((size_t)b * s_q + t) * heads + hd;
-        float* orow = out + ri * kDv;
+        float* obase = out + ((size_t)b * M + row_base) * kDv;
 #pragma unroll
-        for (int ct = 0; ct < kCTiles; ++ct) {
-          float v[16];
-          o_read(ct, v);
-          if (row_ok) {
+        for (int pass = 0; pass < 4; ++pass) {
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-              f32x4 o4 = {v[4 * qd] * inv, v[4 * qd + 1] * inv, v[4 * qd + 2] * inv,
-                          v[4 * qd + 3] * inv};
-              *(f32x4*)(orow + 32 * ct + 8 * qd + 4 * h) = o4;
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const int ct = 4 * pass + c4;
+            float v[16];
+            o_read(ct, v);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 o4 = {v[4 * g] * inv, v[4 * g + 1] * inv, v[4 * g + 2] * inv, v[4 * g + 3] * inv};
+              *(lds_f32x4*)(uintptr_t)(w_off + (32 * c4 + 8 * g) * 4 + 8 * h) = o4;
             }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; i += 4) {
+            u32x4 x[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              x[k] = *(const lds_u32x4*)(uintptr_t)(stage + (2 * (i + k) + rr) * kStagePitch + cl * 16);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int r = 2 * (i + k) + rr;
+              if (row_base + r < M) *(u32x4*)(obase + (size_t)r * kDv + 128 * pass + 4 * cl) = x[k];
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-        if (row_ok && h == 0) lse_out[ri] = lse_v;
+        if (row_ok && h == 0) lse_out[(size_t)b * M + row] = lse_v;
       } else {
-        // One part of a split segment: O_i in fp16 under a power-of-two scale per row that
-        // puts the row's largest |O_i| in [2^14, 2^15), so every value keeps fp16's 11
-        // significant bits and none overflows; the combine multiplies the scale back.
-        // Half the bytes of fp32 partials, written here and read again by the combine.
         const int split = seg == seg_first ? split_first : 0;
         const size_t slot_i = (size_t)seg_slot + split;
-        float amax = 0.f;
+        _Float16* obase = part_o + (slot_i * kGroupRows + wave * 32) * kDv;
 #pragma unroll
-        for (int ct = 0; ct < kCTiles; ++ct) {
-          float v[16];
-          o_read(ct, v);
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) amax = fmaxf(amax, __builtin_fabsf(v[j]));
-        }
-        amax = swap_halves_max(amax) * inv;
-        int e = __builtin_amdgcn_frexp_expf(amax);   // amax in [2^(e-1), 2^e)
-        e = e < -100 ? -100 : (e > 100 ? 100 : e);
-        const float inv_s = inv * __builtin_ldexpf(1.f, 15 - e);
-        _Float16* orow = part_o + (slot_i * kGroupRows + row_in_group) * kDv;
+          for (int c8 = 0; c8 < 8; ++c8) {
+            const int ct = 8 * pass + c8;
+            float v[16];
+            o_read(ct, v);
 #pragma unroll
-        for (int ct = 0; ct < kCTiles; ++ct) {
-          float v[16];
-          o_read(ct, v);
-          if (row_ok) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-              f16x4 o4 = {(_Float16)(v[4 * qd] * inv_s), (_Float16)(v[4 * qd + 1] * inv_s),
-                          (_Float16)(v[4 * qd + 2] * inv_s), (_Float16)(v[4 * qd + 3] * inv_s)};
-              *(f16x4*)(orow + 32 * ct + 8 * qd + 4 * h) = o4;
+            for (int g = 0; g < 4; ++g) {
+              f16x4 o4 = {(_Float16)(v[4 * g] * inv_s), (_Float16)(v[4 * g + 1] * inv_s),
+                          (_Float16)(v[4 * g + 2] * inv_s), (_Float16)(v[4 * g + 3] * inv_s)};
+              *(lds_f16x4*)(uintptr_t)(w_off + (32 * c8 + 8 * g) * 2) = o4;
             }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; i += 4) {
+            u32x4 x[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              x[k] = *(const lds_u32x4*)(uintptr_t)(stage + (2 * (i + k) + rr) * kStagePitch + cl * 16);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int r = 2 * (i + k) + rr;
+              if (row_base + r < M) *(u32x4*)(obase + (size_t)r * kDv + 256 * pass + 8 * cl) = x[k];
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         if (row_ok && h == 0) {
           part_lse[slot_i * kGroupRows + row_in_group] = lse_v;
-          part_scale[slot_i * kGroupRows + row_in_group] = __builtin_ldexpf(1.f, e - 15);
+          part_scale[slot_i * kGroupRows + row_in_group] = __builtin_ldexpf(1.f, pe - 15);
         }
       }
     }
