@@ -125,6 +125,39 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The page copies of bf16 pages set M0 once per window of LDS destinations: a write of
+// M0 stalls the wave while its LDS reads are in flight (~40 cycles in the score loop,
+// measured), so one write per copy cost ~750 cycles per page.  The copy instruction's
+// offset is added to both its LDS address (M0 + offset + 16 * lane) and its global
+// address, so a copy names its LDS destination by a constant offset from the window's
+// M0 and lowers its global base by the same amount.  Nothing between set_m0 and the
+// window's copies writes M0 (the compiler has no use for it in this kernel; the other
+// copy helpers restore it).
+__device__ __forceinline__ void set_m0(uint32_t lds_addr) {
+  lds_addr = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(lds_addr) : "memory", "m0");
+}
+// 16 bytes per lane from sbase + voff into LDS at M0 + kOff + 16 * lane
+template <int kOff>
+__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t voff) {
+  static_assert(kOff >= -4096 && kOff <= 4095 && kOff % 16 == 0, "instruction offset");
+  const uint64_t a = (uint64_t)(uintptr_t)sbase - (uint64_t)(int64_t)kOff;
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const void* base = (const void*)(uintptr_t)((hi << 32) | lo);
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2 nt" ::"v"(voff), "s"(base), "n"(kOff)
+               : "memory");
+}
+// Windows of a wave's 18 copies (rows r0 = 16 * wave ..): main rows r0 .. r0+7 and
+// r0+8 .. r0+15, each window's M0 placed so that the rows' offsets main_row(r) - M0 fall
+// in [-3552, 4080]; then the two tail copies, 1 KiB apart.
+constexpr int kWinCenter = 3552;
+__host__ __device__ constexpr int win_off(int i) {   // row r0 + i relative to its window's M0
+  return 1088 * i + 16 * ((i >> 2) & 3) - (i < 8 ? 0 : 8736) - kWinCenter;
+}
+static_assert(win_off(0) == -3552 && win_off(7) == 4080 && win_off(8) == -3552 &&
+              win_off(15) == 4080, "window offsets");
+
 // 4 bytes per lane from global into LDS at m0 + 4 * lane (the fp8 rows' scales)
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   lds_addr = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
@@ -260,8 +293,8 @@ struct Fp8Lanes {
   uint32_t codes, tail[2], scale;
 };
 
-template <bool kGather, bool kFp8>
-__device__ __forceinline__ void issue_page_part(int i, const PageSrc& src, uint32_t lds_addr,
+template <bool kGather, bool kFp8, int i>
+__device__ __forceinline__ void issue_page_part(const PageSrc& src, uint32_t lds_addr,
                                                 int wave, int lane,
                                                 const uint32_t (&tail_lane_off)[2],
                                                 const GatherRows& g, uint32_t scale_lds,
@@ -285,25 +318,29 @@ __device__ __forceinline__ void issue_page_part(int i, const PageSrc& src, uint3
     return;
   }
   const uint32_t lw = lds_addr + (uint32_t)main_row(r0);
-  if (i < 16) {
+  if constexpr (i == 0) set_m0(lw + kWinCenter);
+  if constexpr (i == 8) set_m0(lw + 8736 + kWinCenter);
+  if constexpr (i == 16) set_m0(lds_addr + kMainBytes + r0 * kTailStride);
+  if constexpr (i < 16) {
+    const char* rsrc;
     if constexpr (kGather) {
-      dma16(src.base + (size_t)(uint32_t)g.ridx[i] * (kDqk * 2), (uint32_t)lane * 16u,
-            lw + main_row(i));
+      rsrc = src.base + (size_t)(uint32_t)g.ridx[i] * (kDqk * 2);
     } else {
       const int rs = r0 + i < vmax ? r0 + i : vmax;
-      dma16(src.base + rs * (kDqk * 2), (uint32_t)lane * 16u, lw + main_row(i));
+      rsrc = src.base + rs * (kDqk * 2);
     }
+    dma16_at<win_off(i)>(rsrc, (uint32_t)lane * 16u);
   } else {
-    const int t = i - 16;
+    constexpr int t = i - 16;
+    uint32_t voff;
     if constexpr (kGather) {
-      dma16(src.base, (uint32_t)g.tail[t] * (uint32_t)(kDqk * 2) + tail_lane_off[t],
-            lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
+      voff = (uint32_t)g.tail[t] * (uint32_t)(kDqk * 2) + tail_lane_off[t];
     } else {
       int row = r0 + 8 * t + (lane >> 3);
       row = row < vmax ? row : vmax;
-      dma16(src.base, (uint32_t)row * (kDqk * 2) + tail_lane_off[t],
-            lds_addr + kMainBytes + (r0 + 8 * t) * kTailStride);
+      voff = (uint32_t)row * (kDqk * 2) + tail_lane_off[t];
     }
+    dma16_at<kTailStride * 8 * t>(src.base, voff);
   }
 }
 constexpr int kPageParts = 18;
@@ -349,9 +386,11 @@ __device__ __forceinline__ void issue_page(const PageSrc& src, uint32_t lds_addr
       return;
     }
   }
-#pragma unroll
-  for (int i = 0; i < (kFp8 ? kFp8Parts : kPageParts); ++i)
-    issue_page_part<kGather, kFp8>(i, src, lds_addr, wave, lane, tail_lane_off, g, scale_lds, f);
+  auto part = [&](auto I) __attribute__((always_inline)) {
+    issue_page_part<kGather, kFp8, decltype(I)::value>(src, lds_addr, wave, lane, tail_lane_off, g,
+                                                       scale_lds, f);
+  };
+  static_for<0, (kFp8 ? kFp8Parts : kPageParts)>(part);
 }
 
 // fp8 pages: widen this wave's 8 row pairs from e4m3 codes to the bf16 main layout in
@@ -719,9 +758,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         kf[s][0] = kfrag(s, 0);
         kf[s][1] = kfrag(s, 1);
       }
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        if (s + kKDepth < kKSteps) {
+      auto score_step = [&](auto S_) __attribute__((always_inline)) {
+        constexpr int s = decltype(S_)::value;
+        if constexpr (s + kKDepth < kKSteps) {
           kf[(s + kKDepth) % (kKDepth + 1)][0] = kfrag(s + kKDepth, 0);
           kf[(s + kKDepth) % (kKDepth + 1)][1] = kfrag(s + kKDepth, 1);
         }
@@ -732,28 +771,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         // the cache) then overlaps that MFMA instead of delaying the LDS reads and MFMAs
         // behind it (~1,100 cycles per page less than issuing it first).
         // (gathered pages: the two tail copies follow the loop)
-        const bool part = (s & 1) == 0 && s / 2 < (kGather ? 16 : (kFp8 ? kFp8Parts : kPageParts));
-        if (s == 0) {
+        constexpr bool part = (s & 1) == 0 && s / 2 < (kGather ? 16 : (kFp8 ? kFp8Parts : kPageParts));
+        if constexpr (s == 0)
           mfma_s_first(sacc[0], a0, qf[s]);
-          if (part) issue_page_part<kGather, kFp8>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
+        else
+          mfma_s(sacc[0], a0, qf[s]);
+        if constexpr (part)
+          issue_page_part<kGather, kFp8, s / 2>(nps, next_lds, wave, lane, tail_lane_off, grows,
+                                                scale_lds, f8l);
+        if constexpr (s == 0)
           mfma_s_first(sacc[1], a1, qf[s]);
-        } else if (s + 1 < kKSteps) {
-          mfma_s(sacc[0], a0, qf[s]);
-          if (part) issue_page_part<kGather, kFp8>(s / 2, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
+        else if constexpr (s + 1 < kKSteps)
           mfma_s(sacc[1], a1, qf[s]);
-        } else {
-          mfma_s(sacc[0], a0, qf[s]);
+        else
           mfma_s_last(sacc[1], a1, qf[s]);
-        }
-
         __builtin_amdgcn_sched_barrier(0);
-      }
+      };
+      static_for<0, kKSteps>(score_step);
       if constexpr (kGather) {
         // each lane's rows for the two tail copies, now that all 16 row numbers are in
         if (nps.load) {
           set_rows();
-          issue_page_part<kGather, kFp8>(16, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
-          issue_page_part<kGather, kFp8>(17, nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
+          issue_page_part<kGather, kFp8, 16>(nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
+          issue_page_part<kGather, kFp8, 17>(nps, next_lds, wave, lane, tail_lane_off, grows, scale_lds, f8l);
         }
       }
       if (blk + 2 < blk_end) {
