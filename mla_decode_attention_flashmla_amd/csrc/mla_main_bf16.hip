@@ -456,8 +456,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     const int32_t* __restrict__ src_row, int64_t num_blocks,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seqlens,
     int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
-    float* __restrict__ lse_out, int32_t* __restrict__ meta, _Float16* __restrict__ part_o,
-    float* __restrict__ part_lse, float* __restrict__ part_scale) {
+    float* __restrict__ lse_out, int32_t* __restrict__ meta, const int32_t* __restrict__ plan,
+    _Float16* __restrict__ part_o, float* __restrict__ part_lse, float* __restrict__ part_scale) {
   // two page buffers; fp8 pages add 1 KiB of row scales
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + (kFp8 ? 1024 : 0)];
   // fp8 pages: the last segment in which some wave met a row scale outside the format,
@@ -477,12 +477,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
   // The header and this slot's row are read together (one round trip): the row lies
   // inside the buffer the host validated for these sizes, and nothing read from it is
   // used before the header check.
-  const int32_t* wrow = meta + kHdrWords + (size_t)slot * kWgWords;
-  const int32_t* segt = meta + kHdrWords + (size_t)kWgWords * nwg;
-  const int h_magic = sload(meta + H_MAGIC), h_batch = sload(meta + H_BATCH);
-  const int h_sq = sload(meta + H_SQ), h_heads = sload(meta + H_HEADS);
-  const int h_causal = sload(meta + H_CAUSAL), h_nwg = sload(meta + H_NUM_WG);
-  const int h_maxb = sload(meta + H_MAX_BLOCKS), groups = sload(meta + H_NUM_GROUPS);
+  // `plan` is the same buffer as `meta`, read-only: this kernel writes only the status
+  // word (through `meta`), which it never reads, so every plan word it reads is loaded
+  // with scalar loads (through `meta` the compiler must use vector loads, each followed by
+  // a wait for every vector memory operation in flight, page copies included).
+  const int32_t* wrow = plan + kHdrWords + (size_t)slot * kWgWords;
+  const int32_t* segt = plan + kHdrWords + (size_t)kWgWords * nwg;
+  const int h_magic = sload(plan + H_MAGIC), h_batch = sload(plan + H_BATCH);
+  const int h_sq = sload(plan + H_SQ), h_heads = sload(plan + H_HEADS);
+  const int h_causal = sload(plan + H_CAUSAL), h_nwg = sload(plan + H_NUM_WG);
+  const int h_maxb = sload(plan + H_MAX_BLOCKS), groups = sload(plan + H_NUM_GROUPS);
   const int seg_first = sload(wrow + W_SEG_BEGIN);
   const int blk_first = sload(wrow + W_BLK_BEGIN);
   const int seg_last = sload(wrow + W_SEG_END);
@@ -644,17 +648,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     // Q fragments: B operand of the score MFMA, k = 16*s + 8*h + j, column = row.  For the
     // first segment they are requested before the first page copy, so waiting for them
     // does not wait for the copy (loads complete in order).
+    // Lanes of rows past the group's end (row_ok false) load row (t, hd) = (0, 0) of the
+    // sequence instead: their scores and outputs are never stored, and the loads need no
+    // per-load branch.
     bf16x8 qf[kKSteps];
     {
       const __bf16* qrow = q + (((size_t)b * s_q + t) * heads + hd) * kDqk + 8 * h;
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        if (row_ok) {
-          qf[s] = *(const bf16x8*)(qrow + 16 * s);
-        } else {
-          qf[s] = (bf16x8){};
-        }
-      }
+      for (int s = 0; s < kKSteps; ++s) qf[s] = *(const bf16x8*)(qrow + 16 * s);
     }
     if (first_seg) {
       PageSrc ps = page_src(seg, L, blk);
@@ -666,8 +667,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       issue_page<kGather, kFp8>(ps, lds0, wave, lane, tail_lane_off, grows, scale_lds, f8l);
       first_seg = false;
     }
+    // The compiler waits for the Q loads here, not at their uses in the score loop:
+    // it cannot see the page copies (issued from asm), so a wait it placed there (for
+    // "all but the later Q loads") would also wait for copies in flight.  Here the
+    // first page's copies are in flight anyway and the page wait follows.
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+v"(qf[s]));
     o_zero();
-    // Q fragments (possibly zeroed by VALU) and O are read by asm MFMAs only after
+    // Q fragments and O (zeroed by VALU) are read by asm MFMAs only after
     // this fence and its wait states
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7" ::: "memory");
@@ -1040,19 +1047,19 @@ hipError_t launch_main_bf16(const Problem& p, hipStream_t stream) {
     hipLaunchKernelGGL((mla_main_bf16_kernel<false, true>), dim3(p.num_wg), dim3(kThreads), 0,
                        stream, (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
                        p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
-                       p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
+                       p.scale, p.out, p.lse, p.meta, p.meta, (_Float16*)p.part_o, p.part_lse,
                        p.part_scale);
   } else if (p.src_row) {
     hipLaunchKernelGGL((mla_main_bf16_kernel<true, false>), dim3(p.num_wg), dim3(kThreads), 0,
                        stream, (const __bf16*)p.q, (const __bf16*)p.kv, p.src_row, p.num_blocks,
                        p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
-                       p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
+                       p.scale, p.out, p.lse, p.meta, p.meta, (_Float16*)p.part_o, p.part_lse,
                        p.part_scale);
   } else {
     hipLaunchKernelGGL((mla_main_bf16_kernel<false, false>), dim3(p.num_wg), dim3(kThreads), 0,
                        stream, (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
                        p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
-                       p.scale, p.out, p.lse, p.meta, (_Float16*)p.part_o, p.part_lse,
+                       p.scale, p.out, p.lse, p.meta, p.meta, (_Float16*)p.part_o, p.part_lse,
                        p.part_scale);
   }
   return hipGetLastError();
