@@ -489,13 +489,28 @@ def percentiles(ms):
             "p90": float(np.percentile(a, 90)), "min": float(a.min()), "max": float(a.max())}
 
 
+def timed_total(step, steps, stream):
+    """`steps` steps back to back on `stream` between two HIP events: total ms."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
 def timed_steps(step, steps, stream, flush=None):
     """Run `steps` steps on `stream` with a HIP event at every step boundary.
 
     Returns (total_ms, per_step_ms).  Without `flush` the steps run back to back and the
-    total is first event to last.  With `flush` (a callable that writes a large scratch
-    buffer, evicting L2 and the memory-side cache) the flush runs between steps outside
-    the events: each step gets its own event pair and the total is their sum."""
+    total is first event to last; every event between two steps adds ~6 us to the step
+    after it (measured), so the headline total is taken by timed_total instead.  With
+    `flush` (a callable that writes a large scratch buffer, evicting L2 and the
+    memory-side cache) the flush runs between steps outside the events: each step gets
+    its own event pair and the total is their sum."""
     import torch
 
     if flush is None:
@@ -674,15 +689,27 @@ def main():
             raise SystemExit("device status flagged an error (graph replay)")
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     wall0 = time.perf_counter()
-    total_ms, per_step = timed_steps(run_step, args.steps, stream, flush)
-    wall = time.perf_counter() - wall0
+    if flush is None:
+        # the timed steps back to back between two events; the per-step distribution
+        # comes from a second pass with an event at every step boundary
+        total_ms = timed_total(run_step, args.steps, stream)
+        wall = time.perf_counter() - wall0
+        _, per_step = timed_steps(run_step, args.steps, stream)
+    else:
+        total_ms, per_step = timed_steps(run_step, args.steps, stream, flush)
+        wall = time.perf_counter() - wall0
     ms_step = total_ms / args.steps
 
     # the dominant kernel alone: the same number of main-kernel launches (the plan stays
-    # valid), each between two events on the stream it is launched on
+    # valid) on the stream they are launched on: back to back between two events for the
+    # average, then once more with an event per launch for the distribution
     def main_only():
         B.decode_main(q, kv, table, lens, scale, out, lse, plan)
-    main_total_ms, main_per = timed_steps(main_only, args.steps, stream, flush)
+    if flush is None:
+        main_total_ms = timed_total(main_only, args.steps, stream)
+        _, main_per = timed_steps(main_only, args.steps, stream)
+    else:
+        main_total_ms, main_per = timed_steps(main_only, args.steps, stream, flush)
     main_avg_us = main_total_ms * 1e3 / args.steps
     B.decode_combine(q, kv, table, lens, scale, out, lse, plan)
     torch.cuda.synchronize()
@@ -736,8 +763,10 @@ def main():
         "alg_flops": flops,
         "roofline_us": t_roof * 1e6,
         "wall_s": wall,
-        "step_us": percentiles(per_step),
-        "main_kernel_us": percentiles(main_per),
+        "step_us": dict(percentiles(per_step), source="an event pair around every step (flushes between)" if args.flush else
+                        "a second pass of the same steps, an event at every step boundary "
+                        "(each adds ~6 us to the step after it)"),
+        "main_kernel_us": dict(percentiles(main_per), source="an event around every launch"),
         "flush": bool(args.flush),
         "clocks": {"before_warmup": clocks_before, "after_timing": clocks_after},
         "roofline": roof,
