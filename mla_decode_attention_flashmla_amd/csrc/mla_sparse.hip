@@ -1,22 +1,29 @@
-// Sparse MLA decode, first form: gather the selected rows, then the paged decode.
+// Sparse MLA decode: the selected rows' packing.
 //
 // The SparseMLA variant of the Triton-TLE talk's performance section reads, out of a
 // long (128K) context, only a selected list of token positions per sequence.  Attention
 // does not depend on the order of its keys, so the selected rows of sequence b are
-// packed, valid ones first and in list order, into blocks of their own:
+// packed, valid ones first and in list order, into packed blocks of 64:
 //
 //   mla_sparse_index_kernel   one workgroup per sequence: which list entries select a
 //                             key (0 <= position < L_b), their packed order (a block
-//                             scan), the pool row of each, and the packed sequence's
-//                             length and block table;
-//   mla_sparse_gather_kernel  one workgroup per 64 packed rows: copies each row (1152
-//                             bytes, 16-byte loads and stores).
+//                             scan), the pool row of each (the last packed block padded
+//                             with its last row), and the packed sequence's length and
+//                             block table.
 //
-// The packed blocks then go through the scheduler, the bf16 main kernel and the
-// combine exactly as a paged cache does.  A position whose block number lies outside
-// the pool turns its packed block's table entry into -1, which the main kernel reports
-// as a bad block (status bit, NaN output); an invalid length becomes packed length -1,
-// which the scheduler reports.
+// The default path stops there: the scheduler plans over the packed lengths and the bf16
+// main kernel reads each packed block as a "gathered page", copying every row straight
+// from the pool through these row numbers, so no row is copied twice.  That kernel forms
+// a row's byte offset from the pool base in 32 bits, so pools of more than
+// kMaxGatherBlocks blocks (4.3 GB) take a copy first: the ABI then also runs
+//
+//   mla_sparse_gather_kernel  one workgroup per 64 packed rows: copies each row (1152
+//                             bytes, 16-byte loads and stores) into packed blocks,
+//
+// which the paged main kernel then reads like any cache.  A position whose block number
+// lies outside the pool turns its packed block's table entry into -1, which the main
+// kernel reports as a bad block (status bit, NaN output); an invalid length becomes
+// packed length -1, which the scheduler reports.
 #include "mla_internal.h"
 #include "mla_decode.h"
 
