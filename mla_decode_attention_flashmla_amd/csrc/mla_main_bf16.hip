@@ -840,22 +840,28 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         m_run = m_new;
       }
       first_page = false;
-      bf16x8 pf[4];
+      // P^T in bf16, one 16-token chunk per PV k-step (chunk 2T + g holds tile T's
+      // accumulator values 8g .. 8g + 7).  Chunk 0 is computed here; each later chunk is
+      // computed inside the PV loop, during the 16 MFMAs of the chunk before it, where
+      // its VALU work runs beside the matrix unit instead of before it.
+      u32x4 pk[4];
+      float ev[8];
+      auto p_exp = [&](int kc, int j) __attribute__((always_inline)) {
+        ev[j] = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + j], scale_log2, -m_run));
+      };
+      auto p_sum = [&](int j) __attribute__((always_inline)) { l_run += ev[j]; };
+      auto p_pack = [&](int kc, int q) __attribute__((always_inline)) {
+        uint32_t t = pack_bf16(ev[2 * q], ev[2 * q + 1]);
+        asm volatile("" : "+v"(t));  // converted here, not merged with the chunk's others
+        pk[kc][q] = t;
+      };
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
+      for (int j = 0; j < 8; ++j) p_exp(0, j);
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          float e[8];
+      for (int j = 0; j < 8; ++j) p_sum(j);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[T][8 * g + j], scale_log2, -m_run));
-            l_run += e[j];
-          }
-          u32x4 pk = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]),
-                      pack_bf16(e[6], e[7])};
-          pf[2 * T + g] = __builtin_bit_cast(bf16x8, pk);
-        }
-      }
+      for (int q = 0; q < 4; ++q) p_pack(0, q);
       // ---- O^T += V^T . P^T ----
       auto vfrag = [&](int i) -> bf16x8 {
         const int kc = i / kCTiles, ct = i % kCTiles;
@@ -890,7 +896,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         // no wait states after the page's last PV MFMA: O^T is next read by VALU or
         // AGPR moves only at a rescale (after the next page's score MFMAs) or in the
         // epilogue, which waits for it
-        o_pv(ct, vf[i % (kVDepth + 1)], pf[kc]);
+        o_pv(ct, vf[i % (kVDepth + 1)], __builtin_bit_cast(bf16x8, pk[kc]));
+        // the next chunk's weights behind this MFMA, at most two VALU instructions per
+        // MFMA: exponentials on the chunk's first 8 MFMAs, sums and packing on the
+        // next 8, the packing done by the 12th, so at least 4 MFMAs separate the last
+        // write of a chunk's P^T from the first MFMA that reads it
+        if constexpr (kc < 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (ct < 8) {
+            p_exp(kc + 1, ct);
+          } else {
+            p_sum(ct - 8);
+            if constexpr (ct < 12) p_pack(kc + 1, ct - 8);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       };
       static_for<0, kPv>(pv_step);
