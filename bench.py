@@ -407,6 +407,101 @@ def run_hbm_ceiling(args):
     print(json.dumps(res), flush=True)
 
 
+def run_power(args):
+    """Socket power at steady load (hwmon): the main kernel launched back to back, the
+    whole step back to back, and the page-copy probe over the same pool (the main
+    kernel's copies without its compute), each for about --power-seconds.  The sensor
+    averages over tens of milliseconds, so only loads that long read true; one JSON line
+    with W, us per launch and mJ per launch for each."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_flashmla_amd import binding as B
+    from mla_decode_attention_flashmla_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("--power measures the bf16 paged workloads")
+    d = I.make_workload(w)
+    dev = torch.device("cuda", 0)
+    q = torch.from_numpy(d["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = torch.from_numpy(d["kv_cache"].view(np.int16)).view(torch.bfloat16).to(dev)
+    table = torch.from_numpy(d["block_table"]).to(dev)
+    lens = torch.from_numpy(d["seqlens"]).to(dev)
+    out = torch.empty((w.batch, w.s_q, w.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.s_q, w.heads), dtype=torch.float32, device=dev)
+    plan = B.alloc_plan(w.batch, w.s_q, w.heads, w.causal, table.shape[1], None, dev)
+    scale = float(d["scale"])
+    stream = torch.cuda.current_stream()
+    B.get_split_metadata(lens, plan)
+
+    def main_only():
+        B.decode_main(q, kv, table, lens, scale, out, lse, plan)
+
+    def step():
+        B.get_split_metadata(lens, plan)
+        B.decode_main(q, kv, table, lens, scale, out, lse, plan)
+        B.decode_combine(q, kv, table, lens, scale, out, lse, plan)
+
+    phases = [("main_kernel", main_only), ("step", step)]
+    probe_path = os.path.join(ROOT, "mla_decode_attention_flashmla_amd", "libmla_probe.so")
+    if os.path.exists(probe_path):
+        plib = ctypes.CDLL(probe_path)
+        plib.mla_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+        nunits = int(d["kv_cache"].shape[0])
+        order = torch.from_numpy(np.random.default_rng(5).permutation(nunits).astype(np.int32)).to(dev)
+        cus = B.device_workgroups(0)
+        sink = torch.zeros(cus * 256, dtype=torch.int32, device=dev)
+
+        def page_copy():
+            rc = plib.mla_probe_page_read(kv.data_ptr(), 73728, 2, order.data_ptr(), nunits, cus,
+                                          sink.data_ptr(), stream.cuda_stream)
+            assert rc == 0, rc
+        phases.append(("page_copy_probe", page_copy))
+
+    res = {"metric": "socket power at steady load", "unit": "W", "workload": w.name,
+           "seconds_per_phase": args.power_seconds, "results": []}
+    for name, fn in phases:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(20):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        n = max(100, int(args.power_seconds / (a.elapsed_time(b) / 20 * 1e-3)))
+        time.sleep(0.3)
+        power = PowerSampler().start()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        power.stop()
+        us = a.elapsed_time(b) / n * 1e3
+        # the sensor lags: the first quarter of the samples is left out
+        smp = power.samples[len(power.samples) // 4:]
+        summ = None
+        if smp:
+            pw = float(np.median(smp))
+            summ = {"median_w": pw, "p10_w": float(np.percentile(smp, 10)),
+                    "p90_w": float(np.percentile(smp, 90)), "samples": len(smp),
+                    "energy_mj_per_launch": pw * us * 1e-3}
+        res["results"].append({"phase": name, "launches": n, "us_per_launch": us, "power": summ})
+        print(f"[power] {res['results'][-1]}", file=sys.stderr, flush=True)
+    cap = PowerSampler()
+    res["cap_w"] = cap._read("power1_cap") if cap.path else None
+    if B.read_status(plan) != 0:
+        raise SystemExit("device status flagged an error")
+    print(json.dumps(res), flush=True)
+
+
 def kernel_hash():
     """Hash of the main kernel's code: its sources with comments and whitespace removed,
     so an edit to comments alone keeps a counter record valid."""
@@ -433,25 +528,127 @@ def measured_traffic(workload):
     return t.get("bytes_per_launch")
 
 
-def gpu_clocks():
-    """Current clocks and power of the visible GPUs as rocm-smi reports them (raw strings,
-    keyed by card); None where rocm-smi is missing or fails.  Sampled outside the timed
-    region."""
-    import subprocess
+def record_traffic(fetch_csv, write_csv, workload):
+    """Write the traffic record (TRAFFIC_FILE) from two rocprofv3 --pmc counter files of the
+    same bench run with --copy-calibration-mib: FETCH_SIZE and WRITE_SIZE per main-kernel
+    dispatch (mean over all but the first, cold one), each scaled by what the counter reads
+    for the calibration copy (the largest copyBuffer dispatch, which moves that many MiB
+    each way).  Runs on the host only."""
+    import csv
 
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout)
-    except Exception:  # pragma: no cover - depends on the host
-        return None
+    def per_kernel(path, counter):
+        main, copy = [], []
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                if "mla_main_bf16_kernel" in r["Kernel_Name"]:
+                    main.append(float(r["Counter_Value"]))
+                elif "copyBuffer" in r["Kernel_Name"]:
+                    copy.append(float(r["Counter_Value"]))
+        if len(main) < 2 or not copy:
+            raise SystemExit(f"{path}: no main-kernel or calibration-copy dispatches")
+        return sum(main[1:]) / (len(main) - 1), max(copy), len(main) - 1
+
+    fetch, copy_fetch, n = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, copy_write, _ = per_kernel(write_csv, "WRITE_SIZE")
+    mib = 512
+    fs, ws = mib * 1024 / copy_fetch, mib * 1024 / copy_write
+    rec = {"kernel": "mla_main_bf16_kernel", "workload": workload, "kernel_hash": kernel_hash(),
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "copy_calibration_mib": mib, "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write,
+           "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+           "read_bytes_per_launch": round(fetch * fs * 1024),
+           "write_bytes_per_launch": round(write * ws * 1024), "dispatches": n}
+    rec["bytes_per_launch"] = rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def gpu_clocks():
+    """Clock levels and socket power of the GPU as sysfs reports them (pp_dpm_sclk and
+    pp_dpm_mclk: the current level is the line marked '*'; hwmon power1_input in W), read
+    from files only: no helper program is started from a process that uses the GPU.  None
+    where the files are missing."""
+    import glob
+
     keep = {}
-    for card, fields in data.items():
-        if not isinstance(fields, dict):
-            continue
-        keep[card] = {k.strip(" :"): v for k, v in fields.items()
-                      if "clock" in k.lower() or "power" in k.lower()}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        card = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+                if cur:
+                    card[name] = cur[0]
+            except OSError:
+                pass
+        for hw in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input")):
+            try:
+                with open(hw) as f:
+                    card["power_w"] = int(f.read()) / 1e6
+            except (OSError, ValueError):
+                pass
+        if card:
+            keep[os.path.basename(os.path.dirname(dev))] = card
     return keep or None
+
+
+class PowerSampler:
+    """Socket power of the GPU (hwmon power1_input, in W) sampled every ~2 ms from a host
+    thread while the timed work runs, with the board's cap (power1_cap).  Reads sysfs only;
+    None where the box exposes no hwmon power file."""
+
+    def __init__(self):
+        import glob
+
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+        self.path = paths[0] if paths else None
+        self.samples = []
+        self._stop = None
+
+    def _read(self, name):
+        with open(os.path.join(os.path.dirname(self.path), name)) as f:
+            return int(f.read()) / 1e6
+
+    def start(self):
+        import threading
+
+        if self.path is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read("power1_input"))
+                except OSError:  # pragma: no cover - depends on the host
+                    return
+                self._stop.wait(0.002)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        if self._stop is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        import numpy as np
+
+        if not self.samples:
+            return None
+        a = np.asarray(self.samples)
+        try:
+            cap = self._read("power1_cap")
+        except OSError:  # pragma: no cover
+            cap = None
+        return {"median": float(np.median(a)), "p90": float(np.percentile(a, 90)),
+                "max": float(a.max()), "cap": cap, "samples": int(a.size),
+                "source": "hwmon power1_input, sampled every ~2 ms"}
 
 
 def host_info():
@@ -600,9 +797,15 @@ def main():
                     help="write 1 GiB of scratch between timed steps, outside the events, so "
                          "no step finds the cache in L2 or the 256 MB memory-side cache")
     ap.add_argument("--no-clocks", action="store_true",
-                    help="do not sample clocks and power with rocm-smi")
+                    help="do not read clocks and power from sysfs")
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="measure the device's read-bandwidth ceiling (probe kernels) instead")
+    ap.add_argument("--power", action="store_true",
+                    help="measure socket power at steady load (main kernel, step, copy probe) instead")
+    ap.add_argument("--power-seconds", type=float, default=1.5)
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from two rocprofv3 --pmc counter files of a "
+                         "run with --copy-calibration-mib 512 (host only, no GPU)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -610,8 +813,14 @@ def main():
               "(the decode runs on a single GPU, with no inter-GPU sharding).", file=sys.stderr)
         sys.exit(2)
 
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, args.workload)
+        return
     if args.hbm_ceiling:
         run_hbm_ceiling(args)
+        return
+    if args.power:
+        run_power(args)
         return
     from mla_decode_attention_flashmla_amd import inputs as I
     if args.workload in I.SPARSE_WORKLOADS:
