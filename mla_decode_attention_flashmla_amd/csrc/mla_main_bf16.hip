@@ -850,16 +850,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         ev[j] = __builtin_amdgcn_exp2f(
             __builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + j], scale_log2, -m_run));
       };
-      auto p_sum = [&](int j) __attribute__((always_inline)) { l_run += ev[j]; };
+      // The row sum adds the weights as the PV MFMAs use them, rounded to bf16 (each
+      // packed half widened back to fp32 by a shift or a mask), so the normalisation
+      // divides by the sum of exactly the weights the products applied: a single visible
+      // key gets weight 1 and O equals its V row.
       auto p_pack = [&](int kc, int q) __attribute__((always_inline)) {
         uint32_t t = pack_bf16(ev[2 * q], ev[2 * q + 1]);
         asm volatile("" : "+v"(t));  // converted here, not merged with the chunk's others
         pk[kc][q] = t;
+        l_run += __uint_as_float(t << 16) + __uint_as_float(t & 0xffff0000u);
       };
 #pragma unroll
       for (int j = 0; j < 8; ++j) p_exp(0, j);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p_sum(j);
 #pragma unroll
       for (int q = 0; q < 4; ++q) p_pack(0, q);
       // ---- O^T += V^T . P^T ----
@@ -897,18 +899,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
         // AGPR moves only at a rescale (after the next page's score MFMAs) or in the
         // epilogue, which waits for it
         o_pv(ct, vf[i % (kVDepth + 1)], __builtin_bit_cast(bf16x8, pk[kc]));
-        // the next chunk's weights behind this MFMA, at most two VALU instructions per
-        // MFMA: exponentials on the chunk's first 8 MFMAs, sums and packing on the
-        // next 8, the packing done by the 12th, so at least 4 MFMAs separate the last
-        // write of a chunk's P^T from the first MFMA that reads it
-        if constexpr (kc < 3) {
+        // the next chunk's weights behind this MFMA: exponentials on the chunk's first 8
+        // MFMAs, packing and row sums on the next 4, so at least 4 MFMAs separate the
+        // last write of a chunk's P^T from the first MFMA that reads it
+        if constexpr (kc < 3 && ct < 12) {
           __builtin_amdgcn_sched_barrier(0);
-          if constexpr (ct < 8) {
+          if constexpr (ct < 8)
             p_exp(kc + 1, ct);
-          } else {
-            p_sum(ct - 8);
-            if constexpr (ct < 12) p_pack(kc + 1, ct - 8);
-          }
+          else
+            p_pack(kc + 1, ct - 8);
         }
         __builtin_amdgcn_sched_barrier(0);
       };

@@ -101,8 +101,9 @@ def test_deterministic():
 
 def test_single_key_returns_that_row():
     # The key's weight is exp2 of the scaled score minus the rounded running max, i.e.
-    # 1 up to the max's rounding; P = 1 exactly in bf16, so O is the row times 1/l with
-    # l within a few ulp of 1.
+    # 1 up to the max's rounding, which is exactly 1 once rounded to bf16 for the
+    # products; the row sum adds those rounded weights, so l = 1 and O is the V row
+    # exactly (P1 of the definition, bit for bit).
     w = I.Workload("one", 3, 1, 128, 1, "bf16", 192, seed=34)
     d = I.make_workload(w)
     announce("single key")
@@ -111,7 +112,7 @@ def test_single_key_returns_that_row():
     kv = I.bf16_bits_to_float32(d["kv_cache"])
     for b in range(3):
         row = kv[d["block_table"][b, 0], 0, :512]
-        np.testing.assert_allclose(out[b, 0], np.broadcast_to(row, (128, 512)), rtol=5e-7, atol=0)
+        assert np.array_equal(out[b, 0], np.broadcast_to(row, (128, 512)))
     ref_o, ref_l = oracle(d)
     assert np.abs(lse - ref_l).max() < 1e-5
 
@@ -129,6 +130,12 @@ def test_uniform_scores_mean_and_log_n():
     # every weight is exactly 1, so only the split parts' fp16 storage rounds: at most half
     # an fp16 ulp of the part's largest |O| (scaled into [2^14, 2^15)), i.e. 2^-11 of it
     assert np.abs(out - ref_o).max() < 2.0 ** -11 * np.abs(ref_o).max() + 1e-6
+    # one workgroup, no split: l is the exact count and only the fp32 accumulation of the
+    # products rounds (1000 terms)
+    out1, lse1, st1, _ = run(d, num_workgroups=1)
+    assert st1 == 0
+    np.testing.assert_allclose(lse1[0], np.log(1000.0), atol=2e-6)
+    assert np.abs(out1 - ref_o).max() < 1e-5 * np.abs(ref_o).max()
 
 
 def test_causal_reduction_on_device():
