@@ -28,7 +28,8 @@
 // into the asm: after the last score MFMA of a page (before VALU reads of the
 // scores), before the first PV MFMA (after VALU writes of P and O), and before
 // the epilogue reads O^T (a rescale reads it only after the next page's score
-// MFMAs, so the PV loop ends without them).
+// MFMAs, so the PV loop ends without them).  Inside the PV loop the later chunks
+// of P are written by VALU at least 4 MFMAs before the first MFMA that reads them.
 //
 // The running max is allowed to lag the true row max by up to 8 (log2 units):
 // O is only rescaled when a page raises some row's max by more than that, so
