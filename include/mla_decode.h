@@ -22,8 +22,10 @@
  * (host) in mla_read_status.  The caller owns all buffers; the library never
  * allocates device memory and keeps no per-call state (mla_decode_fwd_noalloc
  * keeps its plan and partials in the library's static scratch instead).  Inputs
- * are never modified.  All tensors are dense and row-major (a strided view, e.g. q
- * sliced from a wider projection output, must be copied to a dense buffer first):
+ * are never modified.  All tensors are row-major with dense rows; only
+ * mla_decode_fwd_strided lets the (b, t, h) rows of q and out sit a given number of
+ * elements apart (q sliced from a wider projection output, out a view of a wider
+ * buffer).  Other strided views must be copied to a dense buffer first:
  *
  *   q            [batch][s_q][num_heads][576]        dtype (16-byte aligned)
  *   kv_cache     [num_blocks][64][576]               dtype (16-byte aligned)
@@ -130,6 +132,24 @@ int mla_decode_fwd(int dtype, const void* q, const void* kv_cache, int64_t num_b
                    float scale, float* out, float* lse,
                    int32_t* meta, size_t meta_bytes, int num_workgroups,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_fwd with strided rows: row (b, t, h) of q starts at
+ * q + ((b * s_q + t) * num_heads + h) * q_row_stride and its output row at
+ * out + (...) * out_row_stride (elements); every other argument and rule as in
+ * mla_decode_fwd (mla_decode_fwd is this call with strides 576 and 512).  The 576
+ * (512) values of a row are contiguous and start 16-byte aligned: q_row_stride >= 576
+ * and a multiple of 8 (bf16) or 4 (f32), out_row_stride >= 512 and a multiple of 4,
+ * both at most 2^40; otherwise MLA_ERR_INVALID_ARG.  lse stays dense.  The rows are
+ * only read or written at those addresses: the gaps between them are left untouched.
+ */
+int mla_decode_fwd_strided(int dtype, const void* q, int64_t q_row_stride,
+                           const void* kv_cache, int64_t num_blocks,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           const int32_t* seqlens, int batch, int s_q, int num_heads,
+                           int causal, float scale, float* out, int64_t out_row_stride,
+                           float* lse, int32_t* meta, size_t meta_bytes, int num_workgroups,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The two stages of mla_decode_fwd, for callers that time or schedule them

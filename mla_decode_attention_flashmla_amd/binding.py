@@ -36,7 +36,8 @@ D_V = 512
 EXPORTS = ("mla_device_workgroups", "mla_plan_size", "mla_get_split_metadata",
            "mla_decode_fwd", "mla_decode_main", "mla_decode_combine", "mla_sparse_plan_size",
            "mla_decode_sparse_fwd", "mla_fp8_plan_size", "mla_decode_fp8_fwd", "mla_kv_append",
-           "mla_read_status", "mla_status_string", "mla_decode_fwd_noalloc")
+           "mla_read_status", "mla_status_string", "mla_decode_fwd_noalloc",
+           "mla_decode_fwd_strided")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -79,6 +80,9 @@ def load() -> ctypes.CDLL:
                                   c_p]
     lib.mla_decode_fwd_noalloc.argtypes = [c_int, c_p, c_p, c_i64, c_p, c_int, c_p, c_int,
                                            c_int, c_int, c_int, c_f, c_p, c_p, c_int, c_p]
+    lib.mla_decode_fwd_strided.argtypes = [c_int, c_p, c_i64, c_p, c_i64, c_p, c_int, c_p, c_int,
+                                           c_int, c_int, c_int, c_f, c_p, c_i64, c_p, c_p, c_sz,
+                                           c_int, c_p, c_sz, c_p]
     lib.mla_read_status.argtypes = [c_p, c_p, ctypes.POINTER(ctypes.c_int32)]
     lib.mla_status_string.argtypes = [c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -184,6 +188,43 @@ def _decode(fn: str, q, kv_cache, block_table, seqlens, scale: float, out, lse, 
 def decode_fwd(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream=None):
     """mla_decode_fwd: main kernel + LSE combine into out [B,s_q,H,512] and lse [B,s_q,H]."""
     _decode("mla_decode_fwd", q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream)
+
+
+def _row_stride(t, name: str) -> int:
+    """Elements between consecutive (b, t, h) rows of a [B, s_q, H, D] tensor whose rows
+    are each dense and evenly spaced (e.g. a slice [..., :D] of a wider buffer)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    B, s_q, H, D = t.shape
+    rs = t.stride(2) if H > 1 else (t.stride(1) if s_q > 1 else (t.stride(0) if B > 1 else D))
+    for d, expect in ((2, rs), (1, H * rs), (0, s_q * H * rs)):
+        if t.shape[d] > 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: rows must be evenly spaced (strides {t.stride()})")
+    return rs
+
+
+def decode_fwd_strided(q, kv_cache, block_table, seqlens, scale, out, lse, plan,
+                       stream=None) -> None:
+    """mla_decode_fwd_strided: as decode_fwd, with q and out allowed to be row-strided
+    views (each 576- or 512-value row dense, rows evenly spaced, e.g. q = proj[..., :576]
+    of a wider projection output); kv_cache, the tables and lse dense."""
+    lib = load()
+    for name, t in (("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seqlens", seqlens), ("lse", lse)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    q_rs, o_rs = _row_stride(q, "q"), _row_stride(out, "out")
+    B, s_q, H, D = q.shape
+    if (D != D_QK or kv_cache.shape[1:] != (PAGE, D_QK) or block_table.shape[0] != B
+            or tuple(out.shape) != (B, s_q, H, D_V) or tuple(lse.shape) != (B, s_q, H)
+            or kv_cache.dtype != q.dtype):
+        raise ValueError("shape/dtype mismatch with q [B,s_q,H,576], kv [n,64,576]")
+    _check("mla_decode_fwd_strided", lib.mla_decode_fwd_strided(
+        _dtype_code(q), q.data_ptr(), q_rs, kv_cache.data_ptr(), kv_cache.shape[0],
+        block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), B, s_q, H,
+        plan.causal, float(scale), out.data_ptr(), o_rs, lse.data_ptr(), plan.meta.data_ptr(),
+        plan.meta.numel() * 4, plan.num_workgroups, plan.workspace.data_ptr(),
+        plan.workspace.numel(), _stream(stream)))
 
 
 def decode_main(q, kv_cache, block_table, seqlens, scale, out, lse, plan, stream=None):

@@ -91,8 +91,15 @@ int decode(int stages, int dtype, const void* q, const void* kv_cache, int64_t n
            const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens,
            int batch, int s_q, int num_heads, int causal, float scale, float* out, float* lse,
            int32_t* meta, size_t meta_bytes, int num_workgroups, void* workspace,
-           size_t workspace_bytes, void* stream) {
+           size_t workspace_bytes, void* stream, int64_t q_row_stride = kDqk,
+           int64_t out_row_stride = kDv) {
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  // rows of q and out may be strided (q sliced from a wider projection output, out a view
+  // of a wider buffer); every row must start 16-byte aligned
+  const int64_t q_align = dtype == MLA_DTYPE_BF16 ? 8 : 4;
+  if (q_row_stride < kDqk || q_row_stride % q_align != 0 || q_row_stride > ((int64_t)1 << 40) ||
+      out_row_stride < kDv || out_row_stride % 4 != 0 || out_row_stride > ((int64_t)1 << 40))
+    return MLA_ERR_INVALID_ARG;
   int rc = check_sizes(batch, s_q, num_heads, num_workgroups);
   if (rc) return rc;
   if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
@@ -124,6 +131,8 @@ int decode(int stages, int dtype, const void* q, const void* kv_cache, int64_t n
   p.scale = scale;
   p.out = out;
   p.lse = lse;
+  p.q_rs = q_row_stride;
+  p.o_rs = out_row_stride;
   p.meta = meta;
   p.num_wg = num_workgroups;
   const size_t slots = num_slots(batch, s_q, num_heads, num_workgroups);
@@ -162,6 +171,15 @@ extern "C" {
 
 int mla_decode_fwd(MLA_DECODE_ARGS) {
   return decode(kStageMain | kStageCombine, MLA_DECODE_PASS);
+}
+int mla_decode_fwd_strided(int dtype, const void* q, int64_t q_row_stride, const void* kv_cache,
+                           int64_t num_blocks, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
+                           int num_heads, int causal, float scale, float* out,
+                           int64_t out_row_stride, float* lse, int32_t* meta, size_t meta_bytes,
+                           int num_workgroups, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode(kStageMain | kStageCombine, MLA_DECODE_PASS, q_row_stride, out_row_stride);
 }
 int mla_decode_main(MLA_DECODE_ARGS) { return decode(kStageMain, MLA_DECODE_PASS); }
 int mla_decode_combine(MLA_DECODE_ARGS) { return decode(kStageCombine, MLA_DECODE_PASS); }

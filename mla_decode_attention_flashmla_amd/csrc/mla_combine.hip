@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     int batch, int s_q, int heads, int causal, int max_blocks, int nwg, float* __restrict__ out,
     float* __restrict__ lse_out,
     const int32_t* __restrict__ meta, const float* __restrict__ part_o,
-    const float* __restrict__ part_lse, const float* __restrict__ part_scale) {
+    const float* __restrict__ part_lse, const float* __restrict__ part_scale, int64_t o_rs) {
   __shared__ float w_s[kRowsPerBlock][kMaxSplitsLds];
   __shared__ float lse_s[kRowsPerBlock];
   const int seg = blockIdx.x;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   if (!plan_ok) {
     if (!row_ok) return;
     const float nan = __builtin_nanf("");
-    float4* o = (float4*)(out + ri * kDv) + 2 * lane;
+    float4* o = (float4*)(out + ri * o_rs) + 2 * lane;
     o[0] = make_float4(nan, nan, nan, nan);
     o[1] = make_float4(nan, nan, nan, nan);
     if (lane == 0) lse_out[ri] = nan;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     if (!row_ok) return;
     const float fill = s_len < 0 ? __builtin_nanf("") : 0.f;
     float4 v = make_float4(fill, fill, fill, fill);
-    float4* o = (float4*)(out + ri * kDv) + 2 * lane;
+    float4* o = (float4*)(out + ri * o_rs) + 2 * lane;
     o[0] = v;
     o[1] = v;
     if (lane == 0) lse_out[ri] = s_len < 0 ? __builtin_nanf("") : -INFINITY;
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     for (int j = 0; j < kBatch; ++j)
       if (i0 + j < nsplit) add(weight(i0 + j), pa[j], pc[j]);
   }
-  float4* o = (float4*)(out + ri * kDv) + 2 * lane;
+  float4* o = (float4*)(out + ri * o_rs) + 2 * lane;
   o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   if (lane == 0) lse_out[ri] = lse_s[rl];
@@ -187,11 +187,11 @@ hipError_t launch_combine(const Problem& p, hipStream_t stream) {
   if (p.part_half)
     hipLaunchKernelGGL(mla_combine_kernel<true>, grid, dim3(kThreads), 0, stream, p.batch, p.s_q,
                        p.heads, p.causal, p.max_blocks, p.num_wg, p.out, p.lse, p.meta,
-                       p.part_o, p.part_lse, p.part_scale);
+                       p.part_o, p.part_lse, p.part_scale, p.o_rs);
   else
     hipLaunchKernelGGL(mla_combine_kernel<false>, grid, dim3(kThreads), 0, stream, p.batch,
                        p.s_q, p.heads, p.causal, p.max_blocks, p.num_wg, p.out, p.lse, p.meta,
-                       p.part_o, p.part_lse, p.part_scale);
+                       p.part_o, p.part_lse, p.part_scale, p.o_rs);
   return hipGetLastError();
 }
 

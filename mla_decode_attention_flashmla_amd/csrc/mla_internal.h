@@ -65,6 +65,9 @@ struct Problem {
   float scale;
   float* out;
   float* lse;
+  // elements from one (b, t, h) row of q / out to the next (dense: 576 / 512)
+  int64_t q_rs = kDqk;
+  int64_t o_rs = kDv;
   int32_t* meta;
   int num_wg;
   float* part_o;    // [slots][128][512] fp32, or fp16 (part_half) in the first half

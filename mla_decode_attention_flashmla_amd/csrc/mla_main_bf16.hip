@@ -43,7 +43,8 @@
 //             scale), copied as is and widened to the bf16 layout below in LDS before
 //             the page's scores.
 // Every source ends in the same LDS layout, so the products, the softmax and the
-// epilogue are shared.
+// epilogue are shared.  A fourth instantiation, kStrided, is the paged one with q and
+// out rows at strides given at run time instead of the dense 576 / 512.
 //
 // LDS page layout (77824 bytes, two pages double-buffered), for 64 banks of 4 bytes:
 //   main region  columns 0..511 of row r (1024 bytes) at 1088*r + 16*((r>>2)&3).
@@ -451,14 +452,21 @@ __device__ __forceinline__ bool fp8_convert(uint32_t page_lds, uint32_t scale_ld
   return bad;
 }
 
-template <bool kGather, bool kFp8>
+template <bool kGather, bool kFp8, bool kStrided>
 __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv,
     const int32_t* __restrict__ src_row, int64_t num_blocks,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seqlens,
     int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ meta, const int32_t* __restrict__ plan,
-    _Float16* __restrict__ part_o, float* __restrict__ part_lse, float* __restrict__ part_scale) {
+    _Float16* __restrict__ part_o, float* __restrict__ part_lse, float* __restrict__ part_scale,
+    int64_t q_rs_arg, int64_t o_rs_arg) {
+  static_assert(!kStrided || (!kGather && !kFp8), "strided rows: paged bf16 pages only");
+  // rows of q and out q_rs / o_rs elements apart.  The dense instantiations take the row
+  // widths as constants: two more 64-bit values live through the page loop cost scalar
+  // registers there.
+  const int64_t q_rs = kStrided ? q_rs_arg : (int64_t)kDqk;
+  const int64_t o_rs = kStrided ? o_rs_arg : (int64_t)kDv;
   // two page buffers; fp8 pages add 1 KiB of row scales
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + (kFp8 ? 1024 : 0)];
   // fp8 pages: the last segment in which some wave met a row scale outside the format,
@@ -654,7 +662,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
     // per-load branch.
     bf16x8 qf[kKSteps];
     {
-      const __bf16* qrow = q + (((size_t)b * s_q + t) * heads + hd) * kDqk + 8 * h;
+      // row (t, hd) of sequence b is row b*M + row of q, q_rs elements apart
+      const __bf16* qrow = q + ((size_t)b * M + (row_ok ? row : 0)) * q_rs + 8 * h;
 #pragma unroll
       for (int s = 0; s < kKSteps; ++s) qf[s] = *(const bf16x8*)(qrow + 16 * s);
     }
@@ -976,7 +985,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
       const int rr = lane_e >> 5, cl = lane_e & 31;              // read-back: row 2i + rr, chunk cl
       const int row_base = rg * kGroupRows + wave * 32;          // first row of this wave
       if (whole) {
-        float* obase = out + ((size_t)b * M + row_base) * kDv;
+        float* obase = out + ((size_t)b * M + row_base) * o_rs;
 #pragma unroll
         for (int pass = 0; pass < 4; ++pass) {
 #pragma unroll
@@ -1000,7 +1009,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int r = 2 * (i + k) + rr;
-              if (row_base + r < M) *(u32x4*)(obase + (size_t)r * kDv + 128 * pass + 4 * cl) = x[k];
+              if (row_base + r < M) *(u32x4*)(obase + (size_t)r * o_rs + 128 * pass + 4 * cl) = x[k];
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1062,24 +1071,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_main_bf16_kernel(
 }  // namespace
 
 hipError_t launch_main_bf16(const Problem& p, hipStream_t stream) {
+  const bool strided = p.q_rs != kDqk || p.o_rs != kDv;
+  if (strided && (p.fp8 || p.src_row)) return hipErrorInvalidValue;
   if (p.fp8) {
-    hipLaunchKernelGGL((mla_main_bf16_kernel<false, true>), dim3(p.num_wg), dim3(kThreads), 0,
+    hipLaunchKernelGGL((mla_main_bf16_kernel<false, true, false>), dim3(p.num_wg), dim3(kThreads), 0,
                        stream, (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
                        p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
                        p.scale, p.out, p.lse, p.meta, p.meta, (_Float16*)p.part_o, p.part_lse,
-                       p.part_scale);
+                       p.part_scale, p.q_rs, p.o_rs);
   } else if (p.src_row) {
-    hipLaunchKernelGGL((mla_main_bf16_kernel<true, false>), dim3(p.num_wg), dim3(kThreads), 0,
+    hipLaunchKernelGGL((mla_main_bf16_kernel<true, false, false>), dim3(p.num_wg), dim3(kThreads), 0,
                        stream, (const __bf16*)p.q, (const __bf16*)p.kv, p.src_row, p.num_blocks,
                        p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
                        p.scale, p.out, p.lse, p.meta, p.meta, (_Float16*)p.part_o, p.part_lse,
-                       p.part_scale);
+                       p.part_scale, p.q_rs, p.o_rs);
+  } else if (strided) {
+    hipLaunchKernelGGL((mla_main_bf16_kernel<false, false, true>), dim3(p.num_wg),
+                       dim3(kThreads), 0, stream, (const __bf16*)p.q, (const __bf16*)p.kv,
+                       nullptr, p.num_blocks, p.block_table, p.max_blocks, p.seqlens, p.batch,
+                       p.s_q, p.heads, p.causal, p.scale, p.out, p.lse, p.meta, p.meta,
+                       (_Float16*)p.part_o, p.part_lse, p.part_scale, p.q_rs, p.o_rs);
   } else {
-    hipLaunchKernelGGL((mla_main_bf16_kernel<false, false>), dim3(p.num_wg), dim3(kThreads), 0,
-                       stream, (const __bf16*)p.q, (const __bf16*)p.kv, nullptr, p.num_blocks,
-                       p.block_table, p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal,
-                       p.scale, p.out, p.lse, p.meta, p.meta, (_Float16*)p.part_o, p.part_lse,
-                       p.part_scale);
+    hipLaunchKernelGGL((mla_main_bf16_kernel<false, false, false>), dim3(p.num_wg),
+                       dim3(kThreads), 0, stream, (const __bf16*)p.q, (const __bf16*)p.kv,
+                       nullptr, p.num_blocks, p.block_table, p.max_blocks, p.seqlens, p.batch,
+                       p.s_q, p.heads, p.causal, p.scale, p.out, p.lse, p.meta, p.meta,
+                       (_Float16*)p.part_o, p.part_lse, p.part_scale, p.q_rs, p.o_rs);
   }
   return hipGetLastError();
 }

@@ -18,12 +18,17 @@ constexpr int kTok = 32;         // keys per LDS tile
 constexpr int kLd = kDqk + 4;    // padded LDS row (fp32 words): 16-byte rows, rows j and
                                  // j+1 four banks apart for 16-byte reads
 
+// kStrided: q and out rows q_rs / o_rs elements apart; the dense instantiation reads the
+// Q slice as one contiguous run and takes the row widths as constants.
+template <bool kStrided>
 __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kv, int64_t num_blocks,
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seqlens,
     int batch, int s_q, int heads, int causal, float scale, float* __restrict__ out,
     float* __restrict__ lse_out, int32_t* __restrict__ meta, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    float* __restrict__ part_lse, int64_t q_rs_arg, int64_t o_rs_arg) {
+  const int64_t q_rs = kStrided ? q_rs_arg : (int64_t)kDqk;
+  const int64_t o_rs = kStrided ? o_rs_arg : (int64_t)kDv;
   __shared__ __attribute__((aligned(16))) float qs[kRows * kLd];
   __shared__ __attribute__((aligned(16))) float ks[kTok * kLd];
   __shared__ float ps[kRows * kTok];
@@ -81,18 +86,25 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
 
     for (int r0 = 0; r0 < rows_in_group; r0 += kRows) {
       // Q slice -> LDS (rows past M are zero).  Row (t, h) of sequence b is q row
-      // b*M + t*heads + h, so the slice's rows are one contiguous run.
+      // b*M + t*heads + h, q_rs elements after the previous one: dense rows make the
+      // slice one contiguous run.
       {
-        const float4* qsrc =
-            (const float4*)(q + ((size_t)b * M + rg * kGroupRows + r0) * kDqk);
-        const int n_in = min(kRows, rows_in_group - r0) * kDqk / 4;
+        const float* qsrc = q + ((size_t)b * M + rg * kGroupRows + r0) * q_rs;
+        const int n_rows = min(kRows, rows_in_group - r0);
         constexpr int kQVec = kRows * kDqk / 4 / kThreads;
         static_assert(kQVec * 4 * kThreads == kRows * kDqk, "slice split");
         float4 qv[kQVec];
 #pragma unroll
         for (int k = 0; k < kQVec; ++k) {
           const int i = tid + kThreads * k;
-          qv[k] = i < n_in ? qsrc[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (kStrided) {
+            const int r = i / (kDqk / 4), c = i - r * (kDqk / 4);
+            qv[k] = r < n_rows ? *(const float4*)(qsrc + (size_t)r * q_rs + 4 * c)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+          } else {
+            qv[k] = i < n_rows * (kDqk / 4) ? ((const float4*)qsrc)[i]
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
 #pragma unroll
         for (int k = 0; k < kQVec; ++k) {
@@ -238,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
         float* lrow;
         if (nsplit == 1) {
           const size_t ri = ((size_t)b * s_q + t) * heads + hd;
-          orow = out + ri * kDv;
+          orow = out + ri * o_rs;
           lrow = lse_out + ri;
         } else {
           orow = part_o + (slot_i * kGroupRows + row_in_group) * kDv;
@@ -259,10 +271,16 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
 }  // namespace
 
 hipError_t launch_main_f32(const Problem& p, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_main_f32_kernel, dim3(p.num_wg), dim3(kThreads), 0, stream,
-                     (const float*)p.q, (const float*)p.kv, p.num_blocks, p.block_table,
-                     p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal, p.scale, p.out,
-                     p.lse, p.meta, p.part_o, p.part_lse);
+  if (p.q_rs != kDqk || p.o_rs != kDv)
+    hipLaunchKernelGGL(mla_main_f32_kernel<true>, dim3(p.num_wg), dim3(kThreads), 0, stream,
+                       (const float*)p.q, (const float*)p.kv, p.num_blocks, p.block_table,
+                       p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal, p.scale,
+                       p.out, p.lse, p.meta, p.part_o, p.part_lse, p.q_rs, p.o_rs);
+  else
+    hipLaunchKernelGGL(mla_main_f32_kernel<false>, dim3(p.num_wg), dim3(kThreads), 0, stream,
+                       (const float*)p.q, (const float*)p.kv, p.num_blocks, p.block_table,
+                       p.max_blocks, p.seqlens, p.batch, p.s_q, p.heads, p.causal, p.scale,
+                       p.out, p.lse, p.meta, p.part_o, p.part_lse, p.q_rs, p.o_rs);
   return hipGetLastError();
 }
 

@@ -187,10 +187,51 @@ def test_fp8_decode_rejects_bad_arguments_without_touching_hip(lib):
     assert _fp8(lib, batch=0, q=None, out=None) == B.MLA_OK
 
 
+def _fwd_strided(lib, q_rs, o_rs, dtype=B.MLA_DTYPE_BF16):
+    return lib.mla_decode_fwd_strided(dtype, 4096, q_rs, 8192, 4, 12288, 4, 16384, 1, 1, 16, 0,
+                                      0.1, 20480, o_rs, 24576, 28672, 1 << 20, 8, 32768, 1 << 30,
+                                      None)
+
+
+@fake_pointers
+def test_strided_decode_rejects_bad_strides_without_touching_hip(lib):
+    # rows of q and out must be dense, 16-byte aligned, and not overlap
+    assert _fwd_strided(lib, 575, 512) == B.MLA_ERR_INVALID_ARG
+    assert _fwd_strided(lib, 580, 512) == B.MLA_ERR_INVALID_ARG      # bf16: multiple of 8
+    assert _fwd_strided(lib, 576, 511) == B.MLA_ERR_INVALID_ARG
+    assert _fwd_strided(lib, 576, 514) == B.MLA_ERR_INVALID_ARG      # multiple of 4
+    assert _fwd_strided(lib, 576, 1 << 41) == B.MLA_ERR_INVALID_ARG
+    assert _fwd_strided(lib, 578, 512, B.MLA_DTYPE_F32) == B.MLA_ERR_INVALID_ARG   # f32: of 4
+
+    # valid strides pass on to the same validation as mla_decode_fwd (here a plan buffer
+    # too small, so still no HIP call)
+    def small_plan(dtype, q_rs, o_rs):
+        return lib.mla_decode_fwd_strided(dtype, 4096, q_rs, 8192, 4, 12288, 4, 16384, 1, 1, 16,
+                                          0, 0.1, 20480, o_rs, 24576, 28672, 16, 8, 32768,
+                                          1 << 30, None)
+    assert small_plan(B.MLA_DTYPE_BF16, 640, 520) == B.MLA_ERR_PLAN
+    assert small_plan(B.MLA_DTYPE_F32, 580, 512) == B.MLA_ERR_PLAN
+
+
+def test_row_strides_of_views():
+    """The binding derives a row stride from a view whose rows are dense and evenly
+    spaced, and refuses any other layout."""
+    import torch
+
+    assert B._row_stride(torch.zeros((2, 3, 4, 576))[..., :576], "q") == 576
+    assert B._row_stride(torch.zeros((2, 3, 4, 640))[..., :576], "q") == 640
+    assert B._row_stride(torch.zeros((2, 1, 1, 700))[..., 64:640], "q") == 700
+    with pytest.raises(ValueError, match="evenly spaced"):
+        B._row_stride(torch.zeros((2, 3, 5, 576))[:, :, :4], "q")    # gap after each token
+    with pytest.raises(ValueError, match="contiguous"):
+        B._row_stride(torch.zeros((2, 3, 512, 4)).transpose(2, 3), "out")
+
+
 def test_strided_tensors_are_rejected_on_the_host():
-    """The boundary takes dense row-major buffers only (plain pointers, no strides): the
-    binding refuses a strided view, e.g. q sliced out of a wider projection output or a
-    transposed out, before any library call, so a caller must copy it first."""
+    """The dense entry points take dense row-major buffers only (plain pointers, no
+    strides): the binding refuses a strided view, e.g. q sliced out of a wider projection
+    output or a transposed out, before any library call; such a q or out goes through
+    decode_fwd_strided, anything else must be copied first."""
     import torch
 
     qw = torch.zeros((2, 1, 16, 640), dtype=torch.bfloat16)
@@ -211,3 +252,4 @@ def test_strided_tensors_are_rejected_on_the_host():
     with pytest.raises(ValueError, match="contiguous"):
         B.decode_fp8_fwd(q, torch.zeros((4, 64, 656), dtype=torch.uint8), table, lens, 0.1,
                          out, lse, plan)
+

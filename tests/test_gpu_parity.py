@@ -442,3 +442,35 @@ def test_chunked_full_size_workload():
     out, lse, st, _ = run(d)
     assert st == 0 and np.isfinite(out).all() and np.isfinite(lse).all()
     check_every_sequence(out, lse, oracle_one(d), w.batch, "bf16", what="chunk full size")
+
+
+# ---------------------------------------------------------------- strided rows
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nwg,minb", [(None, 0), (40, 1)])
+def test_strided_rows_equal_dense(dtype, nwg, minb):
+    """mla_decode_fwd_strided with q sliced from a wider buffer (NaN in the gap) and out a
+    view of a wider buffer gives the dense call's O and LSE bit for bit, reads nothing
+    from q's gaps and writes nothing into out's."""
+    lens = [2, 63, 64, 65, 700]   # causal: every length covers the s_q = 2 query tokens
+    w = I.Workload("strided", len(lens), 2, 32, max(lens), dtype, 192, causal=True,
+                   ragged=True, seed=46)
+    d = I.make_workload(w, seqlens=lens)
+    announce(f"strided rows {dtype} nwg={nwg} min_split={minb}")
+    t = to_device(d)
+    out_d, lse_d, st, plan = run(d, t, num_workgroups=nwg, min_split_blocks=minb)
+    assert st == 0
+    q_rs = 576 + 64
+    o_rs = 512 + 8
+    qw = torch.full(t["q"].shape[:3] + (q_rs,), float("nan"), dtype=t["q"].dtype, device="cuda")
+    qw[..., 32:32 + 576] = t["q"]
+    ow = torch.full(t["q"].shape[:3] + (o_rs,), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full(t["q"].shape[:3], 7.0, dtype=torch.float32, device="cuda")
+    B.decode_fwd_strided(qw[..., 32:32 + 576], t["kv"], t["table"], t["lens"], float(d["scale"]),
+                         ow[..., 4:4 + 512], lse, plan)
+    assert B.read_status(plan) == 0
+    torch.cuda.synchronize()
+    ow = ow.cpu().numpy()
+    assert np.array_equal(ow[..., 4:4 + 512], out_d)
+    assert np.array_equal(lse.cpu().numpy(), lse_d)
+    assert (ow[..., :4] == 7.0).all() and (ow[..., 4 + 512:] == 7.0).all()

@@ -31,15 +31,18 @@ def asm(tmp_path_factory):
     return out.read_text()
 
 
-# instantiations: <gathered pages, fp8 pages>; the paged one is the hot path
-KINDS = {"paged": "ILb0ELb0E", "gathered": "ILb1ELb0E", "fp8": "ILb0ELb1E"}
+# instantiations: <gathered pages, fp8 pages, strided q / out rows>; the paged one is the
+# hot path
+KINDS = {"paged": "ILb0ELb0ELb0E", "gathered": "ILb1ELb0ELb0E", "fp8": "ILb0ELb1ELb0E",
+         "strided": "ILb0ELb0ELb1E"}
+WHICH = list(range(len(KINDS)))
 
 
 def _kernel_bodies(asm):
-    """The code of each instantiation of the kernel (paged, gathered and fp8 pages), in
-    the order paged, gathered, fp8."""
+    """The code of each instantiation of the kernel (paged, gathered and fp8 pages, paged
+    with strided rows), in the order of KINDS."""
     names = re.findall(r"^(_Z\w*mla_main_bf16_kernel\w*):", asm, re.M)
-    assert len(names) == 3, names
+    assert len(names) == len(KINDS), names
     names = [next(n for n in names if tag in n) for tag in KINDS.values()]
     bodies = []
     for n in names:
@@ -49,19 +52,20 @@ def _kernel_bodies(asm):
 
 
 def test_no_spills_and_full_agpr_file(asm):
-    assert len(re.findall(r"NumAgprs: 256\b", asm)) == 3
-    assert len(re.findall(r"Occupancy: 1\b", asm)) == 3
-    paged, gathered, fp8 = _kernel_bodies(asm)
-    # the paged and gathered kernels never spill; the fp8 one spills a few values, read
-    # back at most once per page
+    assert len(re.findall(r"NumAgprs: 256\b", asm)) == len(KINDS)
+    assert len(re.findall(r"Occupancy: 1\b", asm)) == len(KINDS)
+    paged, gathered, fp8, strided = _kernel_bodies(asm)
+    # the paged, gathered and strided kernels never spill; the fp8 one spills a few
+    # values, read back at most once per page
     assert "scratch_" not in paged and "scratch_" not in gathered
+    assert "scratch_" not in strided
     lines = fp8.splitlines()
     mfma = [k for k, ln in enumerate(lines) if "v_mfma" in ln]
     in_loop = [k for k, ln in enumerate(lines) if "scratch_" in ln and mfma[0] < k < mfma[-1]]
     assert len(in_loop) <= 2, in_loop
 
 
-@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("which", WHICH)
 def test_compiler_code_never_touches_agprs(asm, which):
     inside, bad = False, []
     for ln in _kernel_bodies(asm)[which].splitlines():
@@ -77,7 +81,7 @@ def test_compiler_code_never_touches_agprs(asm, which):
     assert not bad, bad[:5]
 
 
-@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("which", WHICH)
 def test_mfma_count_and_no_packed_fp32(asm, which):
     body = _kernel_bodies(asm)[which]
     # 72 score + 64 PV MFMAs per page, emitted once
@@ -85,7 +89,7 @@ def test_mfma_count_and_no_packed_fp32(asm, which):
     assert not re.search(r"v_pk_(add|mul|fma)_f32", body)
 
 
-@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("which", WHICH)
 def test_valu_writes_are_fenced_before_pv_mfmas(asm, which):
     """Between the scheduling fence before the first PV MFMA and that MFMA, only the
     wait-state nop and LDS/SALU work may appear (no VALU writes of P)."""
@@ -99,7 +103,7 @@ def test_valu_writes_are_fenced_before_pv_mfmas(asm, which):
         assert not code.startswith("v_cvt") and not code.startswith("v_mul"), ln
 
 
-@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("which", WHICH)
 def test_dma_base_address_is_not_sign_extended(asm, which):
     """The 64-bit page base handed to global_load_lds is rebuilt from two readfirstlane
     halves; the low half must be zero-extended (a sign extension turned addresses with
@@ -156,7 +160,7 @@ def test_wait_state_check_sees_a_short_distance():
     assert not _valu_writes_too_close_to_mfma(other)
 
 
-@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("which", WHICH)
 def test_pv_operands_written_by_valu_have_wait_states(asm, which):
     """Inside the PV loop the next chunk's P^T is computed by VALU between the MFMAs that
     read the current one.  An MFMA that reads a VGPR that a VALU instruction wrote needs
@@ -166,7 +170,7 @@ def test_pv_operands_written_by_valu_have_wait_states(asm, which):
     assert not bad, bad[:3]
 
 
-@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("which", WHICH)
 def test_m0_is_set_only_by_the_copy_asm(asm, which):
     """The page copies set M0 (the LDS destination of direct-to-LDS loads) once per window
     of copies in inline asm and rely on it until the window's last copy: code the
