@@ -150,10 +150,19 @@ def alloc_plan(batch: int, s_q: int, heads: int, causal: bool, max_blocks: int,
 
 def get_split_metadata(seqlens, plan: Plan, min_split_blocks: int = 0, stream=None) -> None:
     """mla_get_split_metadata: fill plan.meta from seqlens (int32 device tensor)."""
+    if (tuple(seqlens.shape) != (plan.batch,) or seqlens.dtype != torch_int32()
+            or not seqlens.is_contiguous() or not seqlens.is_cuda
+            or seqlens.device != plan.meta.device):
+        raise ValueError("seqlens must be a contiguous int32 [B] tensor on the plan's GPU")
     _check("mla_get_split_metadata", load().mla_get_split_metadata(
         seqlens.data_ptr(), plan.batch, plan.s_q, plan.heads, plan.causal, plan.max_blocks,
         plan.num_workgroups, min_split_blocks, plan.meta.data_ptr(),
         plan.meta.numel() * 4, _stream(stream)))
+
+
+def torch_int32():
+    import torch
+    return torch.int32
 
 
 def _dtype_code(t) -> int:
@@ -163,6 +172,26 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float32:
         return MLA_DTYPE_F32
     raise MlaError("dtype", MLA_ERR_UNSUPPORTED)
+
+
+def _check_operands(B: int, block_table, seqlens, floats=(), others=(), plan=None) -> None:
+    """What the C ABI cannot see in plain pointers: element types, the lengths of the
+    per-sequence arrays, and that every buffer is GPU memory of one device."""
+    import torch
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    if tuple(seqlens.shape) != (B,) or seqlens.dtype != torch.int32:
+        raise ValueError("seqlens must be int32 [B]")
+    for name, t in floats:
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    ts = [("block_table", block_table), ("seqlens", seqlens), *floats, *others]
+    if plan is not None:
+        ts += [("plan.meta", plan.meta), ("plan.workspace", plan.workspace)]
+    dev = block_table.device
+    for name, t in ts:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"{name} must be in the memory of the GPU that holds block_table")
 
 
 def _decode(fn: str, q, kv_cache, block_table, seqlens, scale: float, out, lse, plan: Plan,
@@ -177,6 +206,8 @@ def _decode(fn: str, q, kv_cache, block_table, seqlens, scale: float, out, lse, 
             or tuple(out.shape) != (B, s_q, H, D_V) or tuple(lse.shape) != (B, s_q, H)
             or kv_cache.dtype != q.dtype):
         raise ValueError("shape/dtype mismatch with q [B,s_q,H,576], kv [n,64,576]")
+    _check_operands(B, block_table, seqlens, (("out", out), ("lse", lse)),
+                    (("q", q), ("kv_cache", kv_cache)), plan)
     _check(fn, getattr(lib, fn)(
         _dtype_code(q), q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
         block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), B, s_q, H,
@@ -219,6 +250,8 @@ def decode_fwd_strided(q, kv_cache, block_table, seqlens, scale, out, lse, plan,
             or tuple(out.shape) != (B, s_q, H, D_V) or tuple(lse.shape) != (B, s_q, H)
             or kv_cache.dtype != q.dtype):
         raise ValueError("shape/dtype mismatch with q [B,s_q,H,576], kv [n,64,576]")
+    _check_operands(B, block_table, seqlens, (("out", out), ("lse", lse)),
+                    (("q", q), ("kv_cache", kv_cache)), plan)
     _check("mla_decode_fwd_strided", lib.mla_decode_fwd_strided(
         _dtype_code(q), q.data_ptr(), q_rs, kv_cache.data_ptr(), kv_cache.shape[0],
         block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), B, s_q, H,
@@ -251,6 +284,8 @@ def decode_fwd_noalloc(q, kv_cache, block_table, seqlens, scale, out, lse, causa
             or tuple(out.shape) != (B, s_q, H, D_V) or tuple(lse.shape) != (B, s_q, H)
             or kv_cache.dtype != q.dtype):
         raise ValueError("shape/dtype mismatch with q [B,s_q,H,576], kv [n,64,576]")
+    _check_operands(B, block_table, seqlens, (("out", out), ("lse", lse)),
+                    (("q", q), ("kv_cache", kv_cache)))
     if num_workgroups is None:
         num_workgroups = device_workgroups(q.device.index or 0)
     _check("mla_decode_fwd_noalloc", lib.mla_decode_fwd_noalloc(
@@ -297,6 +332,10 @@ def decode_sparse_fwd(q, kv_cache, block_table, seqlens, indices, scale, out, ls
             or _dtype_code(q) != MLA_DTYPE_BF16):
         raise ValueError("shape/dtype mismatch with bf16 q [B,1,H,576], kv [n,64,576], "
                          "indices [B,topk]")
+    if indices.dim() != 2 or indices.dtype != torch_int32():
+        raise ValueError("indices must be int32 [B, topk]")
+    _check_operands(B, block_table, seqlens, (("out", out), ("lse", lse)),
+                    (("q", q), ("kv_cache", kv_cache), ("indices", indices)), plan)
     _check("mla_decode_sparse_fwd", lib.mla_decode_sparse_fwd(
         q.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0], block_table.data_ptr(),
         block_table.shape[1], seqlens.data_ptr(), indices.data_ptr(), topk, B, H, float(scale),
@@ -339,6 +378,8 @@ def decode_fp8_fwd(q, kv_fp8, block_table, seqlens, scale, out, lse, plan: Plan,
             or block_table.shape[0] != B or tuple(out.shape) != (B, s_q, H, D_V)
             or tuple(lse.shape) != (B, s_q, H) or _dtype_code(q) != MLA_DTYPE_BF16):
         raise ValueError("shape/dtype mismatch with bf16 q [B,s_q,H,576], kv_fp8 [n,64,656]")
+    _check_operands(B, block_table, seqlens, (("out", out), ("lse", lse)),
+                    (("q", q), ("kv_fp8", kv_fp8)), plan)
     _check("mla_decode_fp8_fwd", lib.mla_decode_fp8_fwd(
         q.data_ptr(), kv_fp8.data_ptr(), kv_fp8.shape[0], block_table.data_ptr(),
         block_table.shape[1], seqlens.data_ptr(), B, s_q, H, plan.causal, float(scale),
@@ -360,6 +401,11 @@ def kv_append(new_kv, kv_cache, block_table, seqlens, status=None, stream=None) 
     if (D != D_QK or kv_cache.shape[1:] != (PAGE, D_QK) or block_table.shape[0] != B
             or seqlens.shape[0] != B or kv_cache.dtype != new_kv.dtype):
         raise ValueError("shape/dtype mismatch with new_kv [B,s_new,576], kv [n,64,576]")
+    if status is not None and (status.dtype != torch_int32() or status.numel() < 1):
+        raise ValueError("status must be an int32 tensor of at least one element")
+    _check_operands(B, block_table, seqlens, (),
+                    (("new_kv", new_kv), ("kv_cache", kv_cache))
+                    + ((("status", status),) if status is not None else ()))
     _check("mla_kv_append", lib.mla_kv_append(
         _dtype_code(new_kv), new_kv.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
         block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), B, s_new,

@@ -253,3 +253,42 @@ def test_strided_tensors_are_rejected_on_the_host():
         B.decode_fp8_fwd(q, torch.zeros((4, 64, 656), dtype=torch.uint8), table, lens, 0.1,
                          out, lse, plan)
 
+
+def test_operand_types_and_devices_are_checked_on_the_host():
+    """The C ABI sees plain pointers: the binding checks what they cannot carry (float32
+    out and lse, int32 tables and lengths of the right count, GPU memory) before any
+    library call, so a float16 out or an int64 length array never reaches a kernel."""
+    import torch
+
+    q = torch.zeros((2, 1, 16, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((4, 64, 576), dtype=torch.bfloat16)
+    table = torch.zeros((2, 2), dtype=torch.int32)
+    lens = torch.zeros(2, dtype=torch.int32)
+    out = torch.zeros((2, 1, 16, 512))
+    lse = torch.zeros((2, 1, 16))
+    plan = B.Plan(torch.zeros(16, dtype=torch.int32), torch.zeros(16, dtype=torch.uint8),
+                  2, 1, 16, 0, 2, 8)
+    bad = [("out", dict(out=out.half()), "out must be float32"),
+           ("lse", dict(lse=lse.double()), "lse must be float32"),
+           ("lens int64", dict(lens=lens.long()), "seqlens must be int32"),
+           ("lens count", dict(lens=torch.zeros(3, dtype=torch.int32)), "seqlens must be int32"),
+           ("table int64", dict(table=table.long()), "block_table must be int32"),
+           ("host memory", {}, "memory of the GPU")]
+    for fn in (B.decode_fwd, B.decode_fwd_strided, B.decode_main):
+        for what, repl, msg in bad:
+            a = dict(q=q, kv=kv, table=table, lens=lens, out=out, lse=lse)
+            a.update(repl)
+            with pytest.raises(ValueError, match=msg):
+                fn(a["q"], a["kv"], a["table"], a["lens"], 0.1, a["out"], a["lse"], plan)
+    with pytest.raises(ValueError, match="seqlens"):
+        B.get_split_metadata(lens.long(), plan)
+    with pytest.raises(ValueError, match="seqlens"):
+        B.get_split_metadata(lens, plan)          # host memory
+    with pytest.raises(ValueError, match="memory of the GPU"):
+        B.decode_fp8_fwd(q, torch.zeros((4, 64, 656), dtype=torch.uint8), table, lens, 0.1,
+                         out, lse, plan)
+    with pytest.raises(ValueError, match="indices must be int32"):
+        B.decode_sparse_fwd(q, kv, table, lens, torch.zeros((2, 64), dtype=torch.int64), 0.1,
+                            out, lse, plan)
+    with pytest.raises(ValueError, match="memory of the GPU"):
+        B.kv_append(torch.zeros((2, 1, 576), dtype=torch.bfloat16), kv, table, lens)
