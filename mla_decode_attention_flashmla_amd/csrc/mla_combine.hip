@@ -18,7 +18,6 @@ namespace {
 constexpr int kRowsPerBlock = 4;  // 64 threads per row, 8 columns per thread
 constexpr int kThreads = 64 * kRowsPerBlock;
 constexpr int kMaxSplitsLds = 1024;
-constexpr int kBatch = 4;         // parts whose O loads are in flight together
 
 // kHalf: the partial O values are fp16 under a power-of-two scale per (part, row),
 // folded here into the part's weight; otherwise fp32.
@@ -30,6 +29,9 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     const float* __restrict__ part_lse, const float* __restrict__ part_scale, int64_t o_rs) {
   __shared__ float w_s[kRowsPerBlock][kMaxSplitsLds];
   __shared__ float lse_s[kRowsPerBlock];
+  // parts whose O loads are in flight together: one round trip merges a row of up to 16
+  // fp16 parts (the 128-row groups of a 16-sequence batch) where 4 at a time took four
+  constexpr int kBatch = kHalf ? 16 : 8;
   const int seg = blockIdx.x;
   // The header words and this segment's row are all read before any of them is tested,
   // so they arrive in one round trip: the row lies inside the buffer the host validated
@@ -89,15 +91,12 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   // this thread's 8 columns of part j's row: 32 bytes of fp32 or 16 bytes of fp16
   const size_t pstride = (size_t)kGroupRows * kDv;  // elements from one part's row to the next's
   const size_t pbase = (slot0 * kGroupRows + row_in_group) * kDv + 8 * lane;
-  float4 pa[kBatch], pc[kBatch];
+  // fp16 parts stay packed (4 registers each) until they are added
+  uint4 raw[kHalf ? kBatch : 1];
+  float4 pa[kHalf ? 1 : kBatch], pc[kHalf ? 1 : kBatch];
   auto load_part = [&](int jslot, int i) {
     if constexpr (kHalf) {
-      const uint4 raw = *(const uint4*)((const _Float16*)part_o + pbase + i * pstride);
-      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-      const f16x2 a = __builtin_bit_cast(f16x2, raw.x), b2 = __builtin_bit_cast(f16x2, raw.y);
-      const f16x2 c = __builtin_bit_cast(f16x2, raw.z), d = __builtin_bit_cast(f16x2, raw.w);
-      pa[jslot] = make_float4((float)a[0], (float)a[1], (float)b2[0], (float)b2[1]);
-      pc[jslot] = make_float4((float)c[0], (float)c[1], (float)d[0], (float)d[1]);
+      raw[jslot] = *(const uint4*)((const _Float16*)part_o + pbase + i * pstride);
     } else {
       pa[jslot] = *(const float4*)(part_o + pbase + i * pstride);
       pc[jslot] = *(const float4*)(part_o + pbase + i * pstride + 4);
@@ -111,11 +110,19 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
       if (j < nsplit) load_part(j, j);
   }
 
-  // weights exp(LSE_i - LSE) for this row, computed by its 64 threads
+  // weights exp(LSE_i - LSE) for this row, computed by its 64 threads; lane i keeps part
+  // i's LSE and scale from the max pass for the sum pass (parts past 64 are read again)
   float mx = -INFINITY;
   bool nan = false;
+  float l0 = -INFINITY, sc0 = 1.f;
+  if (row_ok && lane < nsplit) {
+    l0 = part_lse[(slot0 + lane) * kGroupRows + row_in_group];
+    if constexpr (kHalf) sc0 = part_scale[(slot0 + lane) * kGroupRows + row_in_group];
+    nan = __builtin_isnan(l0);
+    mx = fmaxf(mx, l0);
+  }
   if (row_ok)
-    for (int i = lane; i < nsplit; i += 64) {
+    for (int i = lane + 64; i < nsplit; i += 64) {
       const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
       nan = nan || __builtin_isnan(l);
       mx = fmaxf(mx, l);
@@ -125,8 +132,13 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
   nan = __builtin_amdgcn_ballot_w64(nan) != 0;
   const float base = mx == -INFINITY ? 0.f : mx;
   float sum = 0.f;
+  if (row_ok && lane < nsplit) {
+    const float w = l0 == -INFINITY ? 0.f : expf(l0 - base);
+    w_s[rl][lane] = w * sc0;
+    sum = w;
+  }
   if (row_ok)
-    for (int i = lane; i < nsplit; i += 64) {
+    for (int i = lane + 64; i < nsplit; i += 64) {
       const float l = part_lse[(slot0 + i) * kGroupRows + row_in_group];
       const float w = l == -INFINITY ? 0.f : expf(l - base);
       const float sc = kHalf ? part_scale[(slot0 + i) * kGroupRows + row_in_group] : 1.f;
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     return l == -INFINITY ? 0.f : expf(l - base) * sc;
   };
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add = [&](float w, const float4& a, const float4& c) {
+  auto add4 = [&](float w, const float4& a, const float4& c) {
     acc[0] = fmaf(w, a.x, acc[0]);
     acc[1] = fmaf(w, a.y, acc[1]);
     acc[2] = fmaf(w, a.z, acc[2]);
@@ -159,9 +171,21 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
     acc[6] = fmaf(w, c.z, acc[6]);
     acc[7] = fmaf(w, c.w, acc[7]);
   };
+  auto add = [&](float w, int jslot) {
+    if constexpr (kHalf) {
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      const uint4 r = raw[jslot];
+      const f16x2 a = __builtin_bit_cast(f16x2, r.x), b2 = __builtin_bit_cast(f16x2, r.y);
+      const f16x2 c = __builtin_bit_cast(f16x2, r.z), d = __builtin_bit_cast(f16x2, r.w);
+      add4(w, make_float4((float)a[0], (float)a[1], (float)b2[0], (float)b2[1]),
+           make_float4((float)c[0], (float)c[1], (float)d[0], (float)d[1]));
+    } else {
+      add4(w, pa[jslot], pc[jslot]);
+    }
+  };
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (j < nsplit) add(weight(j), pa[j], pc[j]);
+    if (j < nsplit) add(weight(j), j);
   // further parts, kBatch at a time with all their loads issued first
   for (int i0 = kBatch; i0 < nsplit; i0 += kBatch) {
 #pragma unroll
@@ -169,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(
       if (i0 + j < nsplit) load_part(j, i0 + j);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
-      if (i0 + j < nsplit) add(weight(i0 + j), pa[j], pc[j]);
+      if (i0 + j < nsplit) add(weight(i0 + j), j);
   }
   float4* o = (float4*)(out + ri * o_rs) + 2 * lane;
   o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
