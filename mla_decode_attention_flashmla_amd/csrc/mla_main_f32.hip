@@ -1,4 +1,4 @@
-// MLA decode main kernel for float32 inputs (vector ALU, exact fp32 arithmetic).
+// MLA decode main kernel for float32 inputs (fp32 matrix cores, no rounding of inputs).
 //
 // Same work partition, output and partial conventions as the bf16 MFMA kernel;
 // used where inputs are fp32 and must not be rounded to bf16.  One workgroup
@@ -6,11 +6,20 @@
 //   stage 32 keys (fp32, 576 wide) in LDS -> 16 x 32 scaled scores -> online
 //   softmax per row -> O[16 x 512] += P . V with V = the first 512 key columns.
 // Rows past a sequence's length are never read (zero-filled in LDS).
+//
+// Both products run on v_mfma_f32_16x16x4f32 (fp32 operands, fp32 accumulation).  For
+// a 16 x 16 tile, lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], and holds
+// D[4 (l / 16) + v][l % 16] in its four accumulators.  Scores: wave w sums dims
+// 144w .. 144w + 143 (lane group g = l / 16 takes 36 consecutive dims of them), and the
+// four partial 16 x 32 score blocks are added through LDS.  P . V: wave w owns output
+// columns 128w .. 128w + 127 (8 tiles), lane group g taking keys 8g .. 8g + 7.
 #include "mla_internal.h"
 #include "mla_decode.h"
 
 namespace mla {
 namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRows = 16;        // rows per slice
@@ -32,10 +41,13 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
   __shared__ __attribute__((aligned(16))) float qs[kRows * kLd];
   __shared__ __attribute__((aligned(16))) float ks[kTok * kLd];
   __shared__ float ps[kRows * kTok];
+  __shared__ float sp[4][kRows][kTok];   // each wave's partial scores
   __shared__ float alpha_s[kRows], m_s[kRows], l_s[kRows];
   __shared__ int bad_s;
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;   // MFMA lane: row/column index, k group
   const int nwg = gridDim.x;
   int slot = blockIdx.x;
   if ((nwg & 7) == 0) slot = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
@@ -85,6 +97,26 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
     const int tok_begin = kb * kPage, tok_end = min(ke * kPage, L);
 
     for (int r0 = 0; r0 < rows_in_group; r0 += kRows) {
+      // Keys of a 32-token tile, read into registers one tile ahead (18 float4 per
+      // thread, all in flight at once).  A tile starts on a multiple of 32 tokens, so it
+      // lies in one block: one block number, then 32 consecutive rows of it, one
+      // contiguous run.  Rows at or past the length are zero.
+      constexpr int kVec = kTok * kDqk / 4 / kThreads;
+      static_assert(kVec * 4 * kThreads == kTok * kDqk, "tile split");
+      float4 kreg[kVec];
+      auto load_tile = [&](int t0) {
+        const int id = block_table[(size_t)b * max_blocks + t0 / kPage];
+        const bool ok = id >= 0 && (int64_t)id < num_blocks;
+        if (!ok && tid == 0) bad_s = 1;
+        const float4* src =
+            (const float4*)(kv + ((size_t)(ok ? id : 0) * kPage + (t0 % kPage)) * kDqk);
+        const int n_in = ok ? min(kTok, tok_end - t0) * kDqk / 4 : 0;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          const int i = tid + kThreads * k;
+          kreg[k] = i < n_in ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      };
       // Q slice -> LDS (rows past M are zero).  Row (t, h) of sequence b is q row
       // b*M + t*heads + h, q_rs elements after the previous one: dense rows make the
       // slice one contiguous run.
@@ -106,6 +138,10 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
                                             : make_float4(0.f, 0.f, 0.f, 0.f);
           }
         }
+        // the first key tile's loads go out before the Q slice is stored, so the two
+        // reads overlap (bad_s is cleared by the one thread that sets it, before it can)
+        if (tid == 0) bad_s = 0;
+        if (tok_begin < tok_end) load_tile(tok_begin);
 #pragma unroll
         for (int k = 0; k < kQVec; ++k) {
           const int i = 4 * (tid + kThreads * k);
@@ -114,33 +150,12 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
         }
       }
       if (tid < kRows) { m_s[tid] = -INFINITY; l_s[tid] = 0.f; }
-      if (tid == 0) bad_s = 0;
-      float acc[kRows][2];
+      // O[4 lg + v][128 wave + 16 ct + li] of this slice
+      floatx4 oacc[8];
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) acc[r][0] = acc[r][1] = 0.f;
+      for (int ct = 0; ct < 8; ++ct) oacc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
 
-      // Keys of a 32-token tile, read into registers one tile ahead (18 float4 per
-      // thread, all in flight at once).  A tile starts on a multiple of 32 tokens, so it
-      // lies in one block: one block number, then 32 consecutive rows of it, one
-      // contiguous run.  Rows at or past the length are zero.
-      constexpr int kVec = kTok * kDqk / 4 / kThreads;
-      static_assert(kVec * 4 * kThreads == kTok * kDqk, "tile split");
-      float4 kreg[kVec];
-      auto load_tile = [&](int t0) {
-        const int id = block_table[(size_t)b * max_blocks + t0 / kPage];
-        const bool ok = id >= 0 && (int64_t)id < num_blocks;
-        if (!ok && tid == 0) bad_s = 1;
-        const float4* src =
-            (const float4*)(kv + ((size_t)(ok ? id : 0) * kPage + (t0 % kPage)) * kDqk);
-        const int n_in = ok ? min(kTok, tok_end - t0) * kDqk / 4 : 0;
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-          const int i = tid + kThreads * k;
-          kreg[k] = i < n_in ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      };
-      if (tok_begin < tok_end) load_tile(tok_begin);
       for (int tok0 = tok_begin; tok0 < tok_end; tok0 += kTok) {
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
@@ -150,29 +165,39 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
         }
         if (tok0 + kTok < tok_end) load_tile(tok0 + kTok);
         __syncthreads();
-        // scores: thread -> key j, rows r and r + 8
+        // this wave's partial scores over dims 144 wave + 36 lg + (0 .. 35): keys li and
+        // 16 + li against row li (rows 16 floats apart in LDS are 4 banks apart, so the
+        // 16-byte reads of 16 lanes are conflict-free)
         {
-          // four independent partial sums per row keep the LDS reads and FMAs pipelined
-          const int j = tid & 31, r = tid >> 5;
-          float a0[4] = {0.f, 0.f, 0.f, 0.f}, a1[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-          for (int d = 0; d < kDqk; d += 4) {
-            const float4 k4 = *(const float4*)(ks + j * kLd + d);
-            const float4 x4 = *(const float4*)(qs + r * kLd + d);
-            const float4 y4 = *(const float4*)(qs + (r + 8) * kLd + d);
-            a0[0] = fmaf(x4.x, k4.x, a0[0]);
-            a0[1] = fmaf(x4.y, k4.y, a0[1]);
-            a0[2] = fmaf(x4.z, k4.z, a0[2]);
-            a0[3] = fmaf(x4.w, k4.w, a0[3]);
-            a1[0] = fmaf(y4.x, k4.x, a1[0]);
-            a1[1] = fmaf(y4.y, k4.y, a1[1]);
-            a1[2] = fmaf(y4.z, k4.z, a1[2]);
-            a1[3] = fmaf(y4.w, k4.w, a1[3]);
+          const float* qa = qs + li * kLd + 144 * wave + 36 * lg;
+          const float* kb = ks + li * kLd + 144 * wave + 36 * lg;
+          floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 9; ++c) {
+            const float4 a = *(const float4*)(qa + 4 * c);
+            const float4 k0 = *(const float4*)(kb + 4 * c);
+            const float4 k1 = *(const float4*)(kb + 16 * kLd + 4 * c);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, k0.x, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, k1.x, s1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, k0.y, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, k1.y, s1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, k0.z, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, k1.z, s1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, k0.w, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, k1.w, s1, 0, 0, 0);
           }
-          const float s0 = (a0[0] + a0[1]) + (a0[2] + a0[3]);
-          const float s1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
-          // online softmax: a row's 32 keys sit in 32 consecutive lanes of one wave, so
-          // its max and sum are shuffle reductions over those lanes
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            sp[wave][4 * lg + v][li] = s0[v];
+            sp[wave][4 * lg + v][16 + li] = s1[v];
+          }
+        }
+        __syncthreads();
+        // online softmax: thread -> key j, rows r and r + 8, each score the sum of the four
+        // waves' parts; a row's 32 keys sit in 32 consecutive lanes of one wave, so its max
+        // and sum are shuffle reductions over those lanes
+        {
+          const int j = tid & 31, r = tid >> 5;
           const int tok = tok0 + j;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
@@ -180,7 +205,8 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
             const int row = rg * kGroupRows + r0 + rr;
             const int t = row / heads;
             const int n = causal ? L - s_q + 1 + t : L;
-            const float sv = (tok < n && tok < tok_end) ? (u ? s1 : s0) * scale : -INFINITY;
+            const float dot = ((sp[0][rr][j] + sp[1][rr][j]) + sp[2][rr][j]) + sp[3][rr][j];
+            const float sv = (tok < n && tok < tok_end) ? dot * scale : -INFINITY;
             float mx = sv;
 #pragma unroll
             for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
@@ -203,49 +229,47 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
           }
         }
         __syncthreads();
-        // O += P . V, thread -> columns 2*tid, 2*tid+1
+        // O = alpha O + P . V over this wave's 8 column tiles.  MFMA s of a tile takes keys
+        // 16 (s / 4) + 4 lg + s % 4 in lane group lg: P's as two 16-byte reads, and V's
+        // rows for the four groups 4 rows (16 banks) apart, so the reads are conflict-free.
         {
-          const int c = 2 * tid;
 #pragma unroll
-          for (int r = 0; r < kRows; ++r) {
-            const float a = alpha_s[r];
-            float o0 = acc[r][0] * a, o1 = acc[r][1] * a;
-            for (int j = 0; j < kTok; ++j) {
-              const float p = ps[r * kTok + j];
-              const float2 v2 = *(const float2*)(ks + j * kLd + c);
-              o0 = fmaf(p, v2.x, o0);
-              o1 = fmaf(p, v2.y, o1);
-            }
-            acc[r][0] = o0;
-            acc[r][1] = o1;
+          for (int v = 0; v < 4; ++v) {
+            const float a = alpha_s[4 * lg + v];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) oacc[ct][v] *= a;
           }
+          const float4 pa = *(const float4*)(ps + li * kTok + 4 * lg);
+          const float4 pb = *(const float4*)(ps + li * kTok + 16 + 4 * lg);
+          const float pk[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+          const float* vb = ks + (4 * lg) * kLd + 128 * wave + li;
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8)
+              oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                  pk[s8], vb[(16 * (s8 >> 2) + (s8 & 3)) * kLd + 16 * ct], oacc[ct], 0, 0, 0);
         }
         __syncthreads();
       }
 
-      // epilogue
+      // epilogue: lane (li, lg) of wave w writes rows 4 lg + v, columns 128 w + 16 ct + li
       const int nsplit = sr[S_NSPLIT];
       const bool bad = mismatch || bad_s;
       const int split = seg == seg_first ? split_first : 0;
       const size_t slot_i = (size_t)sr[S_SLOT] + split;
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        if (r0 + r >= rows_in_group) break;
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * lg + v;
+        if (r0 + r >= rows_in_group) continue;
         const int row_in_group = r0 + r;
         const int row = rg * kGroupRows + row_in_group;
         const int t = row / heads, hd = row - t * heads;
         const float l = l_s[r];
-        float o0, o1, lv;
-        if (bad) {
-          o0 = o1 = lv = __builtin_nanf("");
-        } else if (l > 0.f) {
-          o0 = acc[r][0] / l;
-          o1 = acc[r][1] / l;
-          lv = m_s[r] + logf(l);
-        } else {
-          o0 = o1 = 0.f;
-          lv = -INFINITY;
-        }
+        float lv;
+        if (bad) lv = __builtin_nanf("");
+        else if (l > 0.f) lv = m_s[r] + logf(l);
+        else lv = -INFINITY;
         float* orow;
         float* lrow;
         if (nsplit == 1) {
@@ -256,9 +280,15 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
           orow = part_o + (slot_i * kGroupRows + row_in_group) * kDv;
           lrow = part_lse + slot_i * kGroupRows + row_in_group;
         }
-        orow[2 * tid] = o0;
-        orow[2 * tid + 1] = o1;
-        if (tid == 0) *lrow = lv;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          float o;
+          if (bad) o = __builtin_nanf("");
+          else if (l > 0.f) o = oacc[ct][v] / l;
+          else o = 0.f;
+          orow[128 * wave + 16 * ct + li] = o;
+        }
+        if (wave == 0 && li == 0) *lrow = lv;
       }
       if (tid == 0 && bad)
         atomicOr(&meta[H_STATUS], (bad_s ? MLA_STATUS_BAD_BLOCK : 0) |
