@@ -116,10 +116,15 @@ def plan_size(batch: int, s_q: int, heads: int, num_workgroups: int) -> tuple[in
 
 
 def _stream(stream) -> Optional[int]:
+    """The HIP stream handle: the given torch stream's, else the current device's current
+    stream (torch's raw query: the Stream object costs ~3 us of host time per call)."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 @dataclass
@@ -151,8 +156,8 @@ def alloc_plan(batch: int, s_q: int, heads: int, causal: bool, max_blocks: int,
 def get_split_metadata(seqlens, plan: Plan, min_split_blocks: int = 0, stream=None) -> None:
     """mla_get_split_metadata: fill plan.meta from seqlens (int32 device tensor)."""
     if (tuple(seqlens.shape) != (plan.batch,) or seqlens.dtype != torch_int32()
-            or not seqlens.is_contiguous() or not seqlens.is_cuda
-            or seqlens.device != plan.meta.device):
+            or not seqlens.is_contiguous() or seqlens.get_device() < 0
+            or seqlens.get_device() != plan.meta.get_device()):
         raise ValueError("seqlens must be a contiguous int32 [B] tensor on the plan's GPU")
     _check("mla_get_split_metadata", load().mla_get_split_metadata(
         seqlens.data_ptr(), plan.batch, plan.s_q, plan.heads, plan.causal, plan.max_blocks,
@@ -188,9 +193,9 @@ def _check_operands(B: int, block_table, seqlens, floats=(), others=(), plan=Non
     ts = [("block_table", block_table), ("seqlens", seqlens), *floats, *others]
     if plan is not None:
         ts += [("plan.meta", plan.meta), ("plan.workspace", plan.workspace)]
-    dev = block_table.device
+    dev = block_table.get_device()   # -1 for host memory
     for name, t in ts:
-        if not t.is_cuda or t.device != dev:
+        if dev < 0 or t.get_device() != dev:
             raise ValueError(f"{name} must be in the memory of the GPU that holds block_table")
 
 
