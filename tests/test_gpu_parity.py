@@ -99,17 +99,19 @@ def test_deterministic():
 
 # ---------------------------------------------------------------- definitional pins on device
 
-def test_single_key_returns_that_row():
-    # The key's weight is exp2 of the scaled score minus the rounded running max, i.e.
-    # 1 up to the max's rounding, which is exactly 1 once rounded to bf16 for the
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_key_returns_that_row(dtype):
+    # bf16: the key's weight is exp2 of the scaled score minus the rounded running max,
+    # i.e. 1 up to the max's rounding, which is exactly 1 once rounded to bf16 for the
     # products; the row sum adds those rounded weights, so l = 1 and O is the V row
-    # exactly (P1 of the definition, bit for bit).
-    w = I.Workload("one", 3, 1, 128, 1, "bf16", 192, seed=34)
+    # exactly (P1 of the definition, bit for bit).  fp32: the weight is exp(0) = 1 and
+    # the other keys of the tile are masked to weight 0, so again l = 1 and O = V row.
+    w = I.Workload("one", 3, 1, 128, 1, dtype, 192, seed=34)
     d = I.make_workload(w)
-    announce("single key")
+    announce(f"single key {dtype}")
     out, lse, st, _ = run(d)
     assert st == 0
-    kv = I.bf16_bits_to_float32(d["kv_cache"])
+    kv = I.bf16_bits_to_float32(d["kv_cache"]) if dtype == "bf16" else d["kv_cache"]
     for b in range(3):
         row = kv[d["block_table"][b, 0], 0, :512]
         assert np.array_equal(out[b, 0], np.broadcast_to(row, (128, 512)))
@@ -157,28 +159,30 @@ def test_causal_reduction_on_device():
 
 # ---------------------------------------------------------------- edge cases and failures
 
-def test_nan_tail_and_guard_blocks_do_not_leak():
-    w = I.Workload("poison", 4, 2, 128, 300, "bf16", 192, causal=True, ragged=True, seed=37)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_nan_tail_and_guard_blocks_do_not_leak(dtype):
+    w = I.Workload("poison", 4, 2, 128, 300, dtype, 192, causal=True, ragged=True, seed=37)
     lens = [300, 65, 2, 129]
     clean = I.make_workload(w, seqlens=lens, guard_blocks=3)
     dirty = I.make_workload(w, seqlens=lens, guard_blocks=3, poison=True)
-    announce("NaN poison")
+    announce(f"NaN poison {dtype}")
     a = run(clean, min_split_blocks=1, num_workgroups=16)
     b = run(dirty, min_split_blocks=1, num_workgroups=16)
     assert np.isfinite(b[0]).all() and np.isfinite(b[1]).all()
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_zero_length_sequences():
-    w = I.Workload("zero", 4, 1, 128, 200, "bf16", 192, ragged=True, seed=38)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_length_sequences(dtype):
+    w = I.Workload("zero", 4, 1, 128, 200, dtype, 192, ragged=True, seed=38)
     d = I.make_workload(w, seqlens=[0, 200, 0, 64])
-    announce("zero-length sequences")
+    announce(f"zero-length sequences {dtype}")
     ref_o, ref_l = oracle(d)
     for nwg, minb in ((None, 0), (5, 1)):
         out, lse, st, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
         assert st == 0
         assert np.all(out[[0, 2]] == 0) and np.all(np.isneginf(lse[[0, 2]]))
-        check(out, lse, ref_o, ref_l, "bf16", batches=[1, 3], what="zero-length batch")
+        check(out, lse, ref_o, ref_l, dtype, batches=[1, 3], what="zero-length batch")
 
 
 def test_all_empty_batch():
@@ -189,32 +193,34 @@ def test_all_empty_batch():
     assert st == 0 and np.all(out == 0) and np.all(np.isneginf(lse))
 
 
-def test_invalid_lengths_flag_status_and_nan():
-    w = I.Workload("bad", 3, 2, 128, 128, "bf16", 192, causal=True, seed=40)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_invalid_lengths_flag_status_and_nan(dtype):
+    w = I.Workload("bad", 3, 2, 128, 128, dtype, 192, causal=True, seed=40)
     d = I.make_workload(w, seqlens=[128, 64, 64])
     d["seqlens"] = np.array([128, -5, 1], np.int32)     # -5 invalid; 1 < s_q invalid (causal)
-    announce("invalid lengths")
+    announce(f"invalid lengths {dtype}")
     out, lse, st, _ = run(d)
     assert st & B.MLA_STATUS_BAD_SEQLEN
     assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
     assert np.isnan(out[2]).all() and np.isnan(lse[2]).all()
     ref_o, ref_l = O.mla_decode(d["q"][:1], d["kv_cache"], d["block_table"][:1],
-                                d["seqlens"][:1], d["scale"], True)
-    check(out[:1], lse[:1], ref_o, ref_l, "bf16", what="valid sequence next to invalid ones")
+                                d["seqlens"][:1], d["scale"], True, dtype=dtype)
+    check(out[:1], lse[:1], ref_o, ref_l, dtype, what="valid sequence next to invalid ones")
 
 
-def test_bad_block_number_flags_status_and_nan():
-    w = I.Workload("blk", 3, 1, 128, 200, "bf16", 192, seed=41)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bad_block_number_flags_status_and_nan(dtype):
+    w = I.Workload("blk", 3, 1, 128, 200, dtype, 192, seed=41)
     d = I.make_workload(w)
     d["block_table"] = d["block_table"].copy()
     d["block_table"][1, 2] = d["kv_cache"].shape[0] + 5
-    announce("bad block number")
+    announce(f"bad block number {dtype}")
     out, lse, st, _ = run(d, min_split_blocks=1, num_workgroups=8)
     assert st & B.MLA_STATUS_BAD_BLOCK
     # split over several parts: the merged row is NaN in O and in LSE
     assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
     ref_o, ref_l = oracle(d, batches=[0, 2])
-    check(out, lse, ref_o, ref_l, "bf16", batches=[0, 2], what="good sequences")
+    check(out, lse, ref_o, ref_l, dtype, batches=[0, 2], what="good sequences")
 
 
 def test_stale_plan_is_flagged():
