@@ -37,56 +37,86 @@ __global__ __launch_bounds__(kThreads) void mla_sparse_index_kernel(
     int64_t num_blocks, const int32_t* __restrict__ indices, int topk,
     int32_t* __restrict__ src_row, int32_t* __restrict__ packed_len,
     int32_t* __restrict__ packed_table) {
-  __shared__ int wave_tot[kThreads / 64];
+  // Entries are taken in rounds of 256 (thread t: entry 256 k + t of round k), eight rounds
+  // at a time: their list reads, then the block-number reads of the valid ones, all in
+  // flight together.  A valid entry's packed position is the number of valid entries before
+  // it in list order: the totals of earlier rounds, of earlier waves in its round (wave
+  // ballot counts through LDS) and of earlier lanes of its wave (a masked popcount).
+  constexpr int kRounds = 8;
+  constexpr int kWavesPerWg = kThreads / 64;
+  __shared__ int wave_cnt[kRounds][kWavesPerWg];
   __shared__ int bad_chunk[kMaxSparseChunks];
+  __shared__ int32_t last_row;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = seqlens[b];
   const bool len_ok = L >= 0 && (int64_t)L <= (int64_t)max_blocks * kPage;
   const int chunks = topk / kPage;
   for (int c = tid; c < chunks; c += kThreads) bad_chunk[c] = 0;
-
-  // thread tid owns list entries [tid*per, tid*per + per)
-  const int per = topk / kThreads + (topk % kThreads ? 1 : 0);
-  const int e0 = min(topk, tid * per), e1 = min(topk, e0 + per);
   const int32_t* lst = indices + (size_t)b * topk;
-  int run = 0;
-  for (int e = e0; e < e1; ++e) {
-    const int p = lst[e];
-    run += (len_ok && p >= 0 && p < L) ? 1 : 0;
-  }
-  // exclusive block scan of the run lengths
-  int x = run;
+  const int32_t* tab = block_table + (size_t)b * max_blocks;
+  int32_t* dst = src_row + (size_t)b * topk;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes before this one
+  const int rounds = (topk + kThreads - 1) / kThreads;
+  int base = 0;   // valid entries in the rounds already placed
+  for (int r0 = 0; r0 < rounds; r0 += kRounds) {
+    int p[kRounds], blk[kRounds];
+    bool valid[kRounds];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wave_tot[wave] = x;
-  __syncthreads();
-  int before = 0, total = 0;
+    for (int k = 0; k < kRounds; ++k) {
+      const int e = (r0 + k) * kThreads + tid;
+      p[k] = (r0 + k < rounds && e < topk) ? lst[e] : -1;
+    }
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    if (w < wave) before += wave_tot[w];
-    total += wave_tot[w];
+    for (int k = 0; k < kRounds; ++k) {
+      valid[k] = len_ok && p[k] >= 0 && p[k] < L;
+      blk[k] = valid[k] ? tab[p[k] / kPage] : 0;
+    }
+    uint64_t m[kRounds];
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      m[k] = __builtin_amdgcn_ballot_w64(valid[k]);
+      if (lane == 0) wave_cnt[k][wave] = __builtin_popcountll(m[k]);
+    }
+    __syncthreads();
+    int run = base;   // valid entries before round r0 + k
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerWg; ++w) {
+        const int c = wave_cnt[k][w];
+        before += w < wave ? c : 0;
+        total += c;
+      }
+      if (valid[k]) {
+        const int pos = run + before + __builtin_popcountll(m[k] & below);
+        const bool ok = blk[k] >= 0 && (int64_t)blk[k] < num_blocks;
+        const int32_t row = ok ? blk[k] * kPage + p[k] % kPage : -1;
+        dst[pos] = row;
+        if (!ok) bad_chunk[pos / kPage] = 1;
+        p[k] = pos;     // kept for the padding row below
+        blk[k] = row;
+      } else {
+        p[k] = -1;
+      }
+      run += total;
+    }
+    // the entry at position run - 1 is the last valid one so far; a later round with valid
+    // entries overwrites it after the barrier below
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k)
+      if (p[k] >= 0 && p[k] == run - 1) last_row = blk[k];
+    base = run;
+    __syncthreads();   // wave_cnt is reused by the next eight rounds
   }
-  int pos = before + x - run;
-  for (int e = e0; e < e1; ++e) {
-    const int p = lst[e];
-    if (!(len_ok && p >= 0 && p < L)) continue;
-    const int blk = block_table[(size_t)b * max_blocks + p / kPage];
-    const bool ok = blk >= 0 && (int64_t)blk < num_blocks;
-    src_row[(size_t)b * topk + pos] = ok ? blk * kPage + p % kPage : -1;
-    if (!ok) bad_chunk[pos / kPage] = 1;
-    ++pos;
-  }
-  __syncthreads();
+  const int total = base;
   // the rest of the last packed block repeats its last row, so a page read through these
   // lists (the main kernel's gathered pages) only ever addresses real pool rows
   if (total > 0) {
-    const int32_t last = src_row[(size_t)b * topk + total - 1];
+    const int32_t last = last_row;
     const int padded = (total + kPage - 1) / kPage * kPage;
-    for (int e = total + tid; e < padded; e += kThreads) src_row[(size_t)b * topk + e] = last;
+    for (int e = total + tid; e < padded; e += kThreads) dst[e] = last;
   }
   if (tid == 0) packed_len[b] = len_ok ? total : -1;
   for (int c = tid; c < chunks; c += kThreads)
