@@ -70,6 +70,29 @@ def test_sparse_small_cases(heads, context, topk, lens, pad, nwg):
     check(out, lse, ref_o, ref_l, "bf16", what=f"sparse h{heads} k{topk}")
 
 
+def test_sparse_lists_longer_than_eight_rounds():
+    """topk = 4160: 17 rounds of 256 list entries, which the index kernel places eight
+    rounds at a time.  Sequence 0's valid entries are spread over all rounds; sequence
+    1's last list entry is valid (the padding row comes from the final round); sequence
+    2's valid entries all sit in the first 2048 entries, so the later rounds select
+    nothing and the padding row must come from the first eight."""
+    w = I.SparseWorkload("long_list", 3, 32, 6000, 4160, seed=44)
+    d = I.make_sparse_workload(w, seqlens=[6000, 3000, 100], pad=50)
+    idx = d["indices"]
+    ok1 = np.flatnonzero((idx[1] >= 0) & (idx[1] < 3000))
+    idx[1, [ok1[0], -1]] = idx[1, [-1, ok1[0]]]
+    v = idx[2][(idx[2] >= 0) & (idx[2] < 100)]
+    idx[2, :] = -1
+    idx[2, :len(v)] = v
+    assert 0 < len(v) <= 2048 and 0 <= idx[1, -1] < 3000
+    announce("sparse lists of 17 rounds")
+    ref_o, ref_l = oracle(d)
+    for nwg in (None, 11):
+        out, lse, st = run_sparse(d, nwg)
+        assert st == 0
+        check(out, lse, ref_o, ref_l, "bf16", what=f"sparse k4160 nwg={nwg}")
+
+
 def test_sparse_duplicates_and_empty_selection():
     w = I.SparseWorkload("dup", 3, 128, 700, 128, seed=41)
     d = I.make_sparse_workload(w)
