@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void mla_main_f32_kernel(
   const int64_t o_rs = kStrided ? o_rs_arg : (int64_t)kDv;
   __shared__ __attribute__((aligned(16))) float qs[kRows * kLd];
   __shared__ __attribute__((aligned(16))) float ks[kTok * kLd];
-  __shared__ float ps[kRows * kTok];
+  __shared__ __attribute__((aligned(16))) float ps[kRows * kTok];   // read as float4
   __shared__ float sp[4][kRows][kTok];   // each wave's partial scores
   __shared__ float alpha_s[kRows], m_s[kRows], l_s[kRows];
   __shared__ int bad_s;
