@@ -109,7 +109,7 @@ constexpr int kWaveSegs = 64;
 __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
     const int32_t* __restrict__ seqlens, int batch, int s_q, int heads, int causal,
     int max_blocks, int num_wg, int min_split_blocks, int32_t* __restrict__ meta) {
-  __shared__ int32_t l_nblk[kLdsSegs], l_cum[kLdsSegs], l_item[kLdsSegs];
+  __shared__ int32_t l_nblk[kLdsSegs], l_cum[kLdsSegs], l_item[kLdsSegs], l_len[kLdsSegs];
   __shared__ int64_t wave_tot[kThreads / 64];
   __shared__ int status_lds;
   const int tid = threadIdx.x;
@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
         const bool ok = L >= 0 && (int64_t)L <= cap && (!causal || L >= s_q);
         nb = ok ? (L + kPage - 1) / kPage : 0;
         l_nblk[sg] = nb;
+        l_len[sg] = ok ? L : -1;
         int32_t* r = seg + (size_t)sg * kSegWords;
         r[S_NBLK] = nb;
         r[S_SEQLEN] = ok ? L : -1;
@@ -234,6 +235,7 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
       const bool ok = L >= 0 && (int64_t)L <= cap && (!causal || L >= s_q);
       const int nb = ok ? (L + kPage - 1) / kPage : 0;
       NB(s) = nb;
+      if (in_lds) l_len[s] = ok ? L : -1;
       int32_t* r = seg + (size_t)s * kSegWords;
       r[S_NBLK] = nb;
       r[S_SEQLEN] = ok ? L : -1;
@@ -342,6 +344,11 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
   auto parts_al = [&](int s) -> int { return (int)floordiv(NB(s) + c_al - 1, c_al); };
   auto cum_at = [&](int s) { return CUM(s); };
   auto item_at = [&](int s) { return ITEM(s); };
+  // validated length of segment s: from LDS when the segment arrays live there (a read
+  // of the row this kernel just wrote would wait a global round trip)
+  auto len_of = [&](int s) -> int32_t {
+    return in_lds ? l_len[s] : seg[(size_t)s * kSegWords + S_SEQLEN];
+  };
   for (int w = tid; w < num_wg; w += kThreads) {
     int32_t* r = wg + (size_t)w * kWgWords;
     // slot w holds item k iff k*num_wg/n == w for some k
@@ -368,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
       r[W_BLK_END] = (int32_t)floordiv((int64_t)(j + 1) * nb, ps);
       r[W_FIRST_SPLIT] = j;
       r[W_NBLK0] = (int32_t)nb;
-      r[W_SEQLEN0] = seg[(size_t)sb * kSegWords + S_SEQLEN];
+      r[W_SEQLEN0] = len_of(sb);
       continue;
     }
     const int64_t begin = floordiv((int64_t)k * T, n), end = floordiv((int64_t)(k + 1) * T, n);
@@ -380,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void mla_sched_kernel(
     r[W_BLK_END] = (int32_t)(end - CUM(se));
     r[W_FIRST_SPLIT] = (int32_t)(k - item_of(cb, T, n));
     r[W_NBLK0] = NB(sb);
-    r[W_SEQLEN0] = seg[(size_t)sb * kSegWords + S_SEQLEN];
+    r[W_SEQLEN0] = len_of(sb);
   }
 
   if (tid == 0) {
