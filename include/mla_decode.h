@@ -36,7 +36,9 @@
  *   lse          [batch][s_q][num_heads]             float32
  *
  * Streams.  Calls only enqueue work on `stream` (a hipStream_t; NULL is the
- * null stream) and return; none synchronizes except mla_read_status.
+ * null stream) and return; none synchronizes except mla_read_status.  Kernels
+ * launch on the current HIP device: every buffer and `stream` must belong to it
+ * (the library cannot check which device a plain pointer names).
  *
  * Errors.  Every entry point returns MLA_OK (0) or a negative MLA_ERR_* code.
  * Arguments are validated on the host before any HIP call; on error nothing

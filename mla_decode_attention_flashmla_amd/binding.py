@@ -159,6 +159,9 @@ def get_split_metadata(seqlens, plan: Plan, min_split_blocks: int = 0, stream=No
             or not seqlens.is_contiguous() or seqlens.get_device() < 0
             or seqlens.get_device() != plan.meta.get_device()):
         raise ValueError("seqlens must be a contiguous int32 [B] tensor on the plan's GPU")
+    import torch
+    if seqlens.get_device() != torch.cuda.current_device():
+        raise ValueError("seqlens and the plan must be on the current device")
     _check("mla_get_split_metadata", load().mla_get_split_metadata(
         seqlens.data_ptr(), plan.batch, plan.s_q, plan.heads, plan.causal, plan.max_blocks,
         plan.num_workgroups, min_split_blocks, plan.meta.data_ptr(),
@@ -197,6 +200,10 @@ def _check_operands(B: int, block_table, seqlens, floats=(), others=(), plan=Non
     for name, t in ts:
         if dev < 0 or t.get_device() != dev:
             raise ValueError(f"{name} must be in the memory of the GPU that holds block_table")
+    # the library launches on the current device, with these pointers
+    if dev != torch.cuda.current_device():
+        raise ValueError(f"the tensors are on cuda:{dev} but cuda:{torch.cuda.current_device()} "
+                         "is current; call under torch.cuda.device(...)")
 
 
 def _decode(fn: str, q, kv_cache, block_table, seqlens, scale: float, out, lse, plan: Plan,
