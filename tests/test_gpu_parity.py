@@ -140,6 +140,41 @@ def test_uniform_scores_mean_and_log_n():
     assert np.abs(out1 - ref_o).max() < 1e-5 * np.abs(ref_o).max()
 
 
+@pytest.mark.parametrize("trend", ["rising", "falling", "alternating"])
+def test_score_trends_that_force_rescales(trend):
+    """Every head gets the same query q, and key j gets c_j * q / |q|^2 added, so its
+    scaled score moves by scale * c_j for all heads.  Rising by 0.1 per token, each 64-key
+    page's maximum exceeds the previous page's by 6.4 (9.2 in log2 units, past the
+    kernel's slack of 8), so O is rescaled on every page; falling, the first page
+    dominates and later weights underflow; alternating +-20 per page, the running maximum
+    jumps back and forth.  Forced splits make the combine merge parts whose LSEs differ
+    by tens."""
+    L = 1000
+    w = I.Workload("trend", 2, 1, 128, L, "bf16", 192, seed=47)
+    d = I.make_workload(w, seqlens=[L, L - 37])
+    q = I.bf16_bits_to_float32(d["q"])
+    q[:, :, :, :] = q[:, :, :1, :]                       # one query for all heads
+    kv = I.bf16_bits_to_float32(d["kv_cache"])
+    scale = float(d["scale"])
+    j = np.arange(L)
+    shift = {"rising": 0.1 * j, "falling": -0.1 * j,
+             "alternating": np.where((j // 64) % 2 == 0, 20.0, -20.0)}[trend] / scale
+    for b in range(2):
+        qb = q[b, 0, 0].astype(np.float64)
+        u = qb / (qb @ qb)                                # q . (c u) = c
+        for jj in range(int(d["seqlens"][b])):
+            blk, row = d["block_table"][b, jj // 64], jj % 64
+            kv[blk, row] = (kv[blk, row] + shift[jj] * u).astype(np.float32)
+    d["q"] = I.float32_to_bf16_bits(q)
+    d["kv_cache"] = I.float32_to_bf16_bits(kv)
+    announce(f"score trend {trend}")
+    ref_o, ref_l = oracle(d)
+    for nwg, minb in ((None, 0), (16, 1)):
+        out, lse, st, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
+        assert st == 0
+        check(out, lse, ref_o, ref_l, "bf16", what=f"{trend} nwg={nwg}")
+
+
 def test_causal_reduction_on_device():
     """Token 1 of a causal pair equals a 1-query decode at L; token 0 equals one at L-1."""
     w = I.Workload("cr", 3, 2, 128, 500, "bf16", 192, causal=True, seed=36)
