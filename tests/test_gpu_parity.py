@@ -51,6 +51,39 @@ def test_small_cases(heads, s_q, causal, lens, dtype):
         check(out, lse, ref_o, ref_l, dtype, what=f"nwg={nwg} min_split={minb}")
 
 
+def _random_case(i):
+    """Seeded shapes for the sweep below: heads, s_q, causal, lengths (0 and s_q included
+    now and then), workgroup count and forced splits."""
+    rng = np.random.default_rng(900 + i)
+    heads = int(rng.choice([16, 32, 48, 64, 96, 128]))
+    s_q = int(rng.integers(1, 5))
+    causal = bool(rng.integers(0, 2)) if s_q > 1 else bool(rng.integers(0, 2))
+    B = int(rng.integers(1, 4))
+    lo = s_q if causal else 0
+    lens = [int(x) for x in rng.integers(lo, 800, size=B)]
+    if rng.random() < 0.3:
+        lens[int(rng.integers(0, B))] = lo          # a sequence at the shortest valid length
+    nwg = int(rng.choice([1, 3, 17, 64, 256]))
+    minb = int(rng.choice([0, 0, 1, 2]))
+    return heads, s_q, causal, lens, nwg, minb
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("i", range(8))
+def test_random_shapes(i, dtype):
+    """A seeded sweep over shapes, lengths and plans, compared with the oracle in full."""
+    heads, s_q, causal, lens, nwg, minb = _random_case(i)
+    w = I.Workload("rand", len(lens), s_q, heads, max(max(lens), 1), dtype, 192,
+                   causal=causal, ragged=True, seed=950 + i)
+    d = I.make_workload(w, seqlens=lens)
+    announce(f"random {i} {dtype} H={heads} s_q={s_q} causal={causal} lens={lens} "
+             f"nwg={nwg} min_split={minb}")
+    ref_o, ref_l = oracle(d)
+    out, lse, status, _ = run(d, num_workgroups=nwg, min_split_blocks=minb)
+    assert status == 0
+    check(out, lse, ref_o, ref_l, dtype, what=f"random case {i}")
+
+
 def test_tiny_fp32_dense_config():
     """The 1 x 16-head x 256-token fp32 config with a dense (identity-table) cache."""
     d = I.make_workload(I.WORKLOADS["tiny_fp32_dense"])
