@@ -292,3 +292,27 @@ def test_operand_types_and_devices_are_checked_on_the_host():
                             out, lse, plan)
     with pytest.raises(ValueError, match="memory of the GPU"):
         B.kv_append(torch.zeros((2, 1, 576), dtype=torch.bfloat16), kv, table, lens)
+
+
+@fake_pointers
+def test_c_caller_compiles_links_and_gets_the_documented_codes(tmp_path):
+    """A C99 program (tests/abi_from_c.c) built against include/mla_decode.h and linked to
+    the library: the header is C, every declared entry point links, and host-side checks
+    return the documented codes without any GPU call."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(B.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I",
+                    os.path.join(root, "include"), os.path.join(root, "tests", "abi_from_c.c"),
+                    "-o", exe, "-L", lib_dir, "-lmla_decode", "-lm",
+                    "-Wl,-rpath," + lib_dir, "-Wl,-rpath-link,/opt/rocm/lib"],
+                   check=True, capture_output=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failures" in r.stdout
