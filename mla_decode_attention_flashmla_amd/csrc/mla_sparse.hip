@@ -6,10 +6,10 @@
 // packed, valid ones first and in list order, into packed blocks of 64:
 //
 //   mla_sparse_index_kernel   one workgroup per sequence: which list entries select a
-//                             key (0 <= position < L_b), their packed order (a block
-//                             scan), the pool row of each (the last packed block padded
-//                             with its last row), and the packed sequence's length and
-//                             block table.
+//                             key (0 <= position < L_b), their packed order (counts of
+//                             the valid entries before each, from wave ballots), the pool
+//                             row of each (the last packed block padded with its last
+//                             row), and the packed sequence's length and block table.
 //
 // The default path stops there: the scheduler plans over the packed lengths and the bf16
 // main kernel reads each packed block as a "gathered page", copying every row straight
